@@ -1,0 +1,310 @@
+"""Checks that pin the fp64 oracle to facts other than its own code.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError if
+a fact fixed by the mathematics or by the source pages does not hold.  The
+same functions run against the real oracle (tests/test_oracle.py, all must
+pass) and against copies of it with a planted mistake
+(tests/test_oracle_mutants.py, at least one must fail per mistake).
+
+Kinds of pin: hand-derived closed forms (tests/golden/closed_forms.json),
+special cases (one key, causal row 0, constant values, zero scale, a key
+that wins by a margin of 800), bounds, symmetries (key/value permutation,
+shifts), the blockwise merge identity, PyTorch's own CPU fp64 attention and
+autograd as an independent library routine, central finite differences, and
+gradient invariants (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _qkv(seed, B, H, Lq, Lk, d, dv=None):
+    r = _rng(seed)
+    dv = d if dv is None else dv
+    return (r.standard_normal((B, H, Lq, d)), r.standard_normal((B, H, Lk, d)),
+            r.standard_normal((B, H, Lk, dv)))
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(1.0, np.max(np.abs(b)) if b.size else 0.0)
+    assert err <= tol * scale, f"{what}: max err {err:.3e} > {tol:.1e} * {scale:.3g}"
+
+
+# --------------------------------------------------------------------------
+# forward pins
+# --------------------------------------------------------------------------
+
+def pin_golden_forward(oracle):
+    g = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))["forward"]
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    for causal, key in ((False, "noncausal"), (True, "causal")):
+        O, lse = oracle.attn_fwd(q, k, v, g["scale"], causal)
+        _close(O[0, 0], g[key]["O"], 1e-14, f"golden O {key}")
+        _close(lse[0, 0], g[key]["lse"], 1e-14, f"golden lse {key}")
+
+
+def pin_single_key(oracle):
+    q, k, v = _qkv(1, 2, 3, 5, 1, 4)
+    scale = 0.37
+    O, lse = oracle.attn_fwd(q, k, v, scale, False)
+    # One key: its probability is exactly 1, so O is exactly that V row.
+    assert np.array_equal(O, np.broadcast_to(v, O.shape)), "single key must return its V row"
+    want = scale * np.einsum("bhid,bhd->bhi", q, k[:, :, 0, :])
+    _close(lse, want, 1e-14, "single-key lse")
+
+
+def pin_causal_row0(oracle):
+    q, k, v = _qkv(2, 2, 2, 9, 9, 5)
+    scale = 0.8
+    O, lse = oracle.attn_fwd(q, k, v, scale, True)
+    assert np.array_equal(O[:, :, 0, :], v[:, :, 0, :]), "causal row 0 must equal V[0]"
+    want = scale * np.sum(q[:, :, 0, :] * k[:, :, 0, :], axis=-1)
+    _close(lse[:, :, 0], want, 1e-14, "causal row-0 lse")
+
+
+def pin_identity_values(oracle):
+    # V = identity exposes the probability matrix itself: O = P.
+    L, d = 7, 3
+    q, k, _ = _qkv(3, 1, 2, L, L, d)
+    v = np.broadcast_to(np.eye(L), (1, 2, L, L)).copy()
+    for causal in (False, True):
+        P, _ = oracle.attn_fwd(q, k, v, 0.9, causal)
+        _close(P.sum(axis=-1), np.ones(P.shape[:-1]), 1e-14, "softmax rows sum to 1")
+        assert np.all(P >= 0), "probabilities must be non-negative"
+        iu = np.triu_indices(L, 1)
+        upper = P[:, :, iu[0], iu[1]]
+        if causal:
+            assert np.all(upper == 0), "causal: keys after the query get probability 0"
+        else:
+            assert np.all(upper > 0), "non-causal: every key gets a positive weight"
+
+
+def pin_constant_values(oracle):
+    q, k, _ = _qkv(4, 2, 2, 6, 8, 4)
+    c = np.array([1.5, -2.0, 0.25, 3.0])
+    v = np.broadcast_to(c, (2, 2, 8, 4)).copy()
+    for causal in (False, True):
+        O, _ = oracle.attn_fwd(q, k, v, 1.1, causal)
+        _close(O, np.broadcast_to(c, O.shape), 1e-14, "constant V rows are returned")
+
+
+def pin_zero_scale(oracle):
+    q, k, v = _qkv(5, 1, 3, 6, 6, 4)
+    O, lse = oracle.attn_fwd(q, k, v, 0.0, False)
+    _close(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape), 1e-14, "scale 0: mean of V")
+    _close(lse, np.full(lse.shape, math.log(6)), 1e-14, "scale 0: lse = ln n")
+    O, lse = oracle.attn_fwd(q, k, v, 0.0, True)
+    n = np.arange(1, 7)
+    prefix = np.cumsum(v, axis=2) / n[None, None, :, None]
+    _close(O, prefix, 1e-14, "scale 0 causal: prefix mean of V")
+    _close(lse, np.broadcast_to(np.log(n), lse.shape), 1e-14, "scale 0 causal: lse = ln(i+1)")
+
+
+def pin_hardmax(oracle):
+    # Key 2 wins every row by a score margin >= 800: exp(-800) underflows to
+    # exactly 0 in float64, so O is exactly V[2] and lse is that score.
+    d = 2
+    q = np.array([[[[1.0, 0.0], [1.0, 0.0], [1.0, 0.0]]]])
+    k = np.array([[[[0.0, 0.0], [-1.0, 0.0], [900.0, 0.0], [5.0, 0.0]]]])
+    v = np.array([[[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]]]])
+    O, lse = oracle.attn_fwd(q, k, v, 1.0, False)
+    assert np.array_equal(O[0, 0], np.broadcast_to(v[0, 0, 2], (3, d))), "hardmax row"
+    assert np.array_equal(lse[0, 0], np.full(3, 900.0)), "hardmax lse"
+
+
+def pin_bounds(oracle):
+    q, k, v = _qkv(6, 2, 2, 11, 11, 6)
+    scale = 0.6
+    for causal in (False, True):
+        O, lse = oracle.attn_fwd(q, k, v, scale, causal)
+        S = scale * np.einsum("bhid,bhjd->bhij", q, k)
+        i = np.arange(11)[:, None]
+        j = np.arange(11)[None, :]
+        vis = (j <= i) if causal else np.ones((11, 11), bool)
+        Smax = np.where(vis, S, -np.inf).max(axis=-1)
+        n = vis.sum(axis=1)
+        assert np.all(lse >= Smax - 1e-12), "lse >= row max"
+        assert np.all(lse <= Smax + np.log(n) + 1e-12), "lse <= row max + ln n"
+        for r in range(11):
+            vv = v[:, :, vis[r], :]
+            assert np.all(O[:, :, r, :] >= vv.min(axis=2) - 1e-12), "O inside the hull of V"
+            assert np.all(O[:, :, r, :] <= vv.max(axis=2) + 1e-12), "O inside the hull of V"
+
+
+def pin_permutation(oracle):
+    q, k, v = _qkv(7, 1, 2, 5, 9, 3)
+    O, lse = oracle.attn_fwd(q, k, v, 0.7, False)
+    p = _rng(70).permutation(9)
+    O2, lse2 = oracle.attn_fwd(q, k[:, :, p], v[:, :, p], 0.7, False)
+    _close(O2, O, 1e-13, "joint key/value permutation leaves O unchanged")
+    _close(lse2, lse, 1e-13, "joint key/value permutation leaves lse unchanged")
+    pq = _rng(71).permutation(5)
+    O3, lse3 = oracle.attn_fwd(q[:, :, pq], k, v, 0.7, False)
+    _close(O3, O[:, :, pq], 1e-13, "query permutation permutes O")
+    _close(lse3, lse[:, :, pq], 1e-13, "query permutation permutes lse")
+
+
+def pin_shift(oracle):
+    q, k, v = _qkv(8, 1, 2, 6, 6, 4)
+    scale = 0.5
+    c = np.array([0.3, -1.2, 2.0, 0.7])
+    for causal in (False, True):
+        O, lse = oracle.attn_fwd(q, k, v, scale, causal)
+        Ok, lsek = oracle.attn_fwd(q, k + c, v, scale, causal)
+        _close(Ok, O, 1e-13, "adding one vector to every key leaves O unchanged")
+        _close(lsek, lse + scale * (q @ c), 1e-13, "key shift moves lse by scale*q.c")
+        Ov, _ = oracle.attn_fwd(q, k, v + c, scale, causal)
+        _close(Ov, O + c, 1e-13, "adding c to every value row adds c to O")
+
+
+def pin_blockwise_merge(oracle):
+    # Splitting the keys into two blocks: exp(lse) adds up and O is the
+    # exp(lse)-weighted mean of the block outputs (the running-statistics
+    # merge of the blockwise method).
+    q, k, v = _qkv(9, 1, 2, 4, 10, 3)
+    O, lse = oracle.attn_fwd(q, k, v, 0.8, False)
+    Oa, la = oracle.attn_fwd(q, k[:, :, :4], v[:, :, :4], 0.8, False)
+    Ob, lb = oracle.attn_fwd(q, k[:, :, 4:], v[:, :, 4:], 0.8, False)
+    _close(np.logaddexp(la, lb), lse, 1e-13, "lse merges by logaddexp")
+    wa = np.exp(la - lse)[..., None]
+    wb = np.exp(lb - lse)[..., None]
+    _close(wa * Oa + wb * Ob, O, 1e-13, "O merges by exp(lse) weights")
+
+
+def _torch_sdpa(q, k, v, scale, causal):
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v)]
+    O = torch.nn.functional.scaled_dot_product_attention(
+        t[0], t[1], t[2], is_causal=causal, scale=scale)
+    return t, O
+
+
+def pin_torch_sdpa(oracle):
+    cases = [(1, 2, 16, 16, 8, False), (2, 1, 13, 13, 4, True), (1, 2, 5, 12, 6, False),
+             (1, 1, 12, 5, 3, True), (1, 1, 7, 19, 5, True)]
+    for n, (B, H, Lq, Lk, d, causal) in enumerate(cases):
+        q, k, v = _qkv(100 + n, B, H, Lq, Lk, d)
+        scale = 1.0 / math.sqrt(d)
+        with torch.no_grad():
+            _, Ot = _torch_sdpa(q, k, v, scale, causal)
+        O, _ = oracle.attn_fwd(q, k, v, scale, causal)
+        _close(O, Ot.numpy(), 1e-12, f"torch fp64 sdpa case {n}")
+
+
+def pin_rows_consistency(oracle):
+    q, k, v = _qkv(10, 1, 2, 20, 20, 4)
+    rows = np.array([[[0, 19, 7, 3], [5, 0, 19, 11]]])
+    for causal in (False, True):
+        O, lse = oracle.attn_fwd(q, k, v, 0.4, causal)
+        Or, lr = oracle.attn_fwd_rows(q, k, v, 0.4, causal, rows)
+        for h in range(2):
+            _close(Or[0, h], O[0, h, rows[0, h]], 1e-14, "sampled rows equal full rows")
+            _close(lr[0, h], lse[0, h, rows[0, h]], 1e-14, "sampled lse equal full lse")
+
+
+# --------------------------------------------------------------------------
+# backward pins
+# --------------------------------------------------------------------------
+
+def pin_golden_backward(oracle):
+    g = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))["backward"]
+    arr = lambda x: np.array(x)[None, None]
+    dq, dk, dv = oracle.attn_bwd(arr(g["q"]), arr(g["k"]), arr(g["v"]), arr(g["dO"]),
+                                 g["scale"], False)
+    _close(dq[0, 0], g["dq"], 1e-14, "golden dq")
+    _close(dk[0, 0], g["dk"], 1e-14, "golden dk")
+    _close(dv[0, 0], g["dv"], 1e-14, "golden dv")
+
+
+def pin_finite_differences(oracle):
+    # Central differences of the loss <dO, O> in float64, step 1e-6.
+    for causal, (Lq, Lk) in ((False, (4, 6)), (True, (5, 5))):
+        q, k, v = _qkv(11 + causal, 1, 1, Lq, Lk, 3)
+        dO = _rng(20 + causal).standard_normal((1, 1, Lq, 3))
+        scale = 0.9
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dO, scale, causal)
+        loss = lambda a, b, c: float(np.sum(dO * oracle.attn_fwd(a, b, c, scale, causal)[0]))
+        h = 1e-6
+        for name, x, grad in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy(); xp[idx] += h
+                xm = x.copy(); xm[idx] -= h
+                args_p = [q, k, v]; args_m = [q, k, v]
+                pos = {"dq": 0, "dk": 1, "dv": 2}[name]
+                args_p[pos] = xp; args_m[pos] = xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(grad, num, 2e-7, f"finite differences {name} causal={causal}")
+
+
+def pin_torch_autograd(oracle):
+    cases = [(1, 2, 9, 9, 4, True), (2, 1, 6, 11, 5, False), (1, 1, 17, 17, 8, True)]
+    for n, (B, H, Lq, Lk, d, causal) in enumerate(cases):
+        q, k, v = _qkv(200 + n, B, H, Lq, Lk, d)
+        dO = _rng(300 + n).standard_normal((B, H, Lq, d))
+        scale = 1.0 / math.sqrt(d)
+        t, Ot = _torch_sdpa(q, k, v, scale, causal)
+        Ot.backward(torch.tensor(dO))
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dO, scale, causal)
+        _close(dq, t[0].grad.numpy(), 1e-12, f"torch autograd dq case {n}")
+        _close(dk, t[1].grad.numpy(), 1e-12, f"torch autograd dk case {n}")
+        _close(dv, t[2].grad.numpy(), 1e-12, f"torch autograd dv case {n}")
+
+
+def pin_gradient_invariants(oracle):
+    q, k, v = _qkv(12, 2, 2, 10, 10, 4)
+    dO = _rng(13).standard_normal((2, 2, 10, 4))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dO, 0.7, causal)
+        # Shifting every key by one vector changes no output: sum_j dK_j = 0.
+        _close(dk.sum(axis=2), np.zeros((2, 2, 4)), 1e-13, "sum of dK over keys is 0")
+        # Rows of P sum to one: sum_j dV_j = sum_i dO_i.
+        _close(dv.sum(axis=2), dO.sum(axis=2), 1e-13, "sum of dV equals sum of dO")
+
+
+def pin_constant_values_backward(oracle):
+    q, k, _ = _qkv(14, 1, 2, 7, 7, 3)
+    v = np.broadcast_to(np.array([2.0, -1.0, 0.5]), (1, 2, 7, 3)).copy()
+    dO = _rng(15).standard_normal((1, 2, 7, 3))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dO, 0.9, causal)
+        # O no longer depends on Q or K.
+        _close(dq, np.zeros_like(dq), 1e-13, "constant V: dQ = 0")
+        _close(dk, np.zeros_like(dk), 1e-13, "constant V: dK = 0")
+
+
+def pin_bwd_heads_consistency(oracle):
+    q, k, v = _qkv(16, 2, 3, 8, 8, 4)
+    dO = _rng(17).standard_normal((2, 3, 8, 4))
+    full = oracle.attn_bwd(q, k, v, dO, 0.5, True)
+    heads = [(1, 2), (0, 0), (1, 0)]
+    part = oracle.attn_bwd_heads(q, k, v, dO, 0.5, True, heads)
+    for n, (b, h) in enumerate(heads):
+        for a, f in zip(part, full):
+            _close(a[n], f[b, h], 1e-14, "per-head backward equals full backward")
+
+
+FORWARD_PINS = [pin_golden_forward, pin_single_key, pin_causal_row0, pin_identity_values,
+                pin_constant_values, pin_zero_scale, pin_hardmax, pin_bounds,
+                pin_permutation, pin_shift, pin_blockwise_merge, pin_torch_sdpa,
+                pin_rows_consistency]
+BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
+                 pin_gradient_invariants, pin_constant_values_backward,
+                 pin_bwd_heads_consistency]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS

@@ -1,0 +1,100 @@
+"""Plant one plausible mistake at a time in the oracle and require that at
+least one pin catches it.  This shows the pins constrain every step of the
+oracle (scale, mask, normaliser, softmax, value product and each gradient
+term), not just its overall shape.  CPU only; the real oracle is restored
+after every case by pytest's monkeypatch."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as A
+from tests import oracle_pins
+
+
+def _bwd_variant(change):
+    """A copy of the per-head backward with one term altered by ``change``."""
+    def head_backward(q, k, v, dO, scale, vis):
+        O, _, P = A._head_forward(q, k, v, scale, vis)
+        t = dict(P=P, O=O, q=q, k=k, v=v, dO=dO, scale=scale)
+        D = change.get("D", lambda t: (t["dO"] * t["O"]).sum(axis=1))(t)
+        t["D"] = D
+        dv = change.get("dv", lambda t: t["P"].T @ t["dO"])(t)
+        dP = change.get("dP", lambda t: t["dO"] @ t["v"].T)(t)
+        t["dP"] = dP
+        dS = change.get("dS", lambda t: t["P"] * (t["dP"] - t["D"][:, None]))(t)
+        t["dS"] = dS
+        dq = change.get("dq", lambda t: t["scale"] * (t["dS"] @ t["k"]))(t)
+        dk = change.get("dk", lambda t: t["scale"] * (t["dS"].T @ t["q"]))(t)
+        return dq, dk, dv
+    return head_backward
+
+
+FORWARD_MUTANTS = {
+    "scale dropped": ("_scores", lambda q, k, s: q @ k.T),
+    "scale squared": ("_scores", lambda q, k, s: s * s * (q @ k.T)),
+    "mask keeps keys after the query": (
+        "visible_mask", lambda Lq, Lk, c: (np.arange(Lk)[None] >= np.arange(Lq)[:, None])
+        if c else np.ones((Lq, Lk), bool)),
+    "mask hides the diagonal": (
+        "visible_mask", lambda Lq, Lk, c: (np.arange(Lk)[None] < np.arange(Lq)[:, None])
+        | (np.arange(Lq)[:, None] == 0) & (np.arange(Lk)[None] == 0)
+        if c else np.ones((Lq, Lk), bool)),
+    "masked scores set to 0 instead of -inf": ("_apply_mask", lambda S, vis: np.where(vis, S, 0.0)),
+    "lse in base 2": ("_row_logsumexp", lambda S: np.log2(np.exp(S).sum(axis=1))),
+    "lse missing the row max": (
+        "_row_logsumexp", lambda S: np.log(np.exp(S - S.max(1, keepdims=True)).sum(axis=1))),
+    "lse without max shift": ("_row_logsumexp", lambda S: np.log(np.exp(S).sum(axis=1))),
+    "softmax not normalised": ("_probabilities", lambda S, lse: np.exp(S)),
+    "softmax over the wrong axis": (
+        "_probabilities", lambda S, lse: np.exp(S - np.log(np.exp(S).sum(axis=0, keepdims=True)))),
+    "values taken reversed": (
+        "_head_forward", lambda q, k, v, s, vis: (lambda O, l, P: (P @ v[::-1], l, P))(
+            *_real_head_forward(q, k, v, s, vis))),
+}
+
+BACKWARD_MUTANTS = {
+    "D term dropped": {"D": lambda t: 0 * t["O"][:, 0]},
+    "D from dO only": {"D": lambda t: t["dO"].sum(axis=1)},
+    "dV without transpose": {"dv": lambda t: t["P"] @ t["dO"]},
+    "dS sign flipped": {"dS": lambda t: t["P"] * (t["D"][:, None] - t["dP"])},
+    "dS missing P factor": {"dS": lambda t: t["dP"] - t["D"][:, None]},
+    "dQ missing scale": {"dq": lambda t: t["dS"] @ t["k"]},
+    "dK missing scale": {"dk": lambda t: t["dS"].T @ t["q"]},
+    "dQ uses values instead of keys": {"dq": lambda t: t["scale"] * (t["dS"] @ t["v"])},
+    "dK from dS without transpose": {"dk": lambda t: t["scale"] * (t["dS"] @ t["q"])},
+    "dP from reversed values": {"dP": lambda t: t["dO"] @ t["v"][::-1].T},
+}
+
+_real_head_forward = A._head_forward
+
+
+def _failures(pins):
+    failed = []
+    for pin in pins:
+        try:
+            pin(oracle)
+        except (AssertionError, ValueError, FloatingPointError, IndexError) as e:
+            failed.append(f"{pin.__name__}: {e}")
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(FORWARD_MUTANTS))
+def test_forward_mutant_is_caught(name, monkeypatch):
+    attr, fn = FORWARD_MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.ALL_PINS)
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(A, "_head_backward", _bwd_variant(BACKWARD_MUTANTS[name]))
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.BACKWARD_PINS)
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _failures(oracle_pins.ALL_PINS) == []
