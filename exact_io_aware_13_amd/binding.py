@@ -1,0 +1,148 @@
+"""Python binding of libfa with the C ABI's names.
+
+``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_workspace_bytes`` only marshal torch
+tensors (device pointers, sizes, the current HIP stream) into the C calls;
+all arithmetic runs in the library's HIP kernels.  PyTorch supplies device
+memory and streams.  ``attention`` wraps both calls in an autograd Function
+with the signature of the annotated-code page's usage example,
+``(q, k, v, causal, scale)`` on [B, H, L, d] tensors, where an omitted scale
+is 1/sqrt(d) ("How Flash Attention Improves Transformer Memory Efficiency
+...", section "Basic Flash Attention Forward Pass").
+"""
+
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.FA_F32, torch.bfloat16: _lib.FA_BF16}
+
+
+def _code(dtype):
+    try:
+        return _DTYPES[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}; libfa takes float32 or bfloat16") from None
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _check_tensor(name, t, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous ([B,H,L,d] row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out_dtype=None, out=None, lse=None):
+    """O, lse = attention(q, k, v) through libfa's ``fa_fwd``.
+
+    q [B,H,Lq,d], k and v [B,H,Lk,d]: contiguous, on one GPU, float32 or
+    bfloat16.  ``out_dtype`` defaults to the input dtype (float32 is allowed
+    for bfloat16 inputs).  Returns (O [B,H,Lq,d], lse [B,H,Lq] float32).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    _check_tensor("k", k, dev, q.dtype, (B, H, Lk, d))
+    _check_tensor("v", v, dev, q.dtype, (B, H, Lk, d))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=out_dtype, device=dev)
+    _check_tensor("out", out, dev, out_dtype, (B, H, Lq, d))
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    lib = _lib.load()
+    st = lib.fa_fwd(_code(q.dtype), _code(out_dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
+                    float(scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
+def fa_bwd_workspace_bytes(dtype, B, H, Lq, Lk, d):
+    """Bytes of workspace ``fa_bwd`` needs (0 for sizes it would reject)."""
+    return int(_lib.load().fa_bwd_workspace_bytes(_code(dtype), B, H, Lq, Lk, d))
+
+
+def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+           workspace=None):
+    """dQ, dK, dV through libfa's ``fa_bwd``.
+
+    o and lse are the forward's outputs (o in the input dtype), do the
+    gradient of o.  ``workspace`` (a uint8 device tensor) is allocated here
+    when not given.  Returns (dq, dk, dv) in the input dtype.
+    """
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
+                         ("o", o, (B, H, Lq, d)), ("do", do, (B, H, Lq, d))):
+        _check_tensor(name, t, dev, q.dtype, shp)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, dev, q.dtype, ref.shape)
+    need = fa_bwd_workspace_bytes(q.dtype, B, H, Lq, Lk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    lib = _lib.load()
+    st = lib.fa_bwd(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                    _ptr(lse), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                    _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return dq, dk, dv
+
+
+class FlashAttentionFn(torch.autograd.Function):
+    """Autograd wrapper: forward saves O and lse, backward calls fa_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = fa_fwd(q, k, v, scale=scale, causal=causal)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = fa_bwd(q, k, v, o, do.contiguous(), lse, scale=ctx.scale, causal=ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal=False, scale=None):
+    """Exact attention on [B, H, L, d] tensors; differentiable.
+
+    ``scale`` defaults to 1/sqrt(d); ``causal`` hides key j from query row i
+    when j > i.
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return FlashAttentionFn.apply(q.contiguous(), k.contiguous(), v.contiguous(), bool(causal),
+                                  float(scale))

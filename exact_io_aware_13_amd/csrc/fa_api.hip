@@ -1,0 +1,144 @@
+// C ABI of libfa (declared in include/fa.h): argument validation, workspace
+// layout and dispatch to the gfx950 kernels.  Validation runs entirely on
+// the host and returns before any HIP call, so an invalid call enqueues
+// nothing.
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxSliceBytes = int64_t(1) << 31;  // per-slice byte offsets stay 32-bit
+
+bool valid_dtype(int t) { return t == FA_F32 || t == FA_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks shared by forward, backward and workspace sizing.  Slices get
+// one tile of slack so that in-kernel offsets of the last (ragged) tile stay
+// representable.
+fa_status check_shape(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d) {
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d <= 0) return FA_ERR_SHAPE;
+  if (B * H > 0 && Lq > 0 && Lk == 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t slack = 256;
+  const int64_t esz = 4;  // fp32 outputs and accumulators bound every path
+  if ((Lq + slack) * d * esz >= kMaxSliceBytes || (Lk + slack) * d * esz >= kMaxSliceBytes)
+    return FA_ERR_SHAPE;
+  if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  // Row counts bound the grids of the row-wise helper kernels.
+  if (bh * Lq > (int64_t(1) << 34) || bh * Lk > (int64_t(1) << 34)) return FA_ERR_SHAPE;
+  const int64_t rows_per_block =
+      in_dtype == FA_BF16 ? fa::kFwdBf16RowsPerBlock : fa::kF32RowsPerBlock;
+  // Grid sizes (x dimension) of the largest launch must fit.
+  if (bh * cdiv(Lq, rows_per_block) > INT32_MAX || bh * cdiv(Lk, fa::kF32RowsPerBlock) > INT32_MAX)
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or too large sizes (negative size, Lk = 0 with Lq > 0, or over 2^31 bytes per slice)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension or dtype combination not implemented (d must be 64 or 128)";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_ARG: return "FA_ERR_ARG: non-finite scale or unknown enum value";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_version(void) { return "libfa 0.1.0 gfx950"; }
+
+fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype, int64_t B, int64_t H, int64_t Lq,
+                 int64_t Lk, int64_t d, const void* Q, const void* K, const void* V, float scale,
+                 int causal, void* O, float* lse, hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  if (in_dtype == FA_F32 && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (B * H * Lq == 0) return FA_OK;
+  if (!Q || !K || !V || !O || !lse) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+
+  fa::FwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lse = lse;
+  a.BH = (int)(B * H);
+  a.Lq = (int)Lq;
+  a.Lk = (int)Lk;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.out_f32 = out_dtype == FA_F32;
+  const hipError_t e = in_dtype == FA_BF16 ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_f32(a, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                              int64_t d) {
+  if (!valid_dtype(in_dtype) || check_shape(in_dtype, B, H, Lq, Lk, d) != FA_OK) return 0;
+  const size_t rows = (size_t)(B * H * Lq);
+  size_t bytes = round_up(rows * sizeof(float), 256);  // D statistic
+  if (in_dtype == FA_BF16) bytes += rows * (size_t)d * sizeof(float);  // fp32 dQ accumulator
+  return bytes;
+}
+
+fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* lse, float scale, int causal, void* dQ, void* dK, void* dV,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  const bool has_q = B * H * Lq > 0, has_k = B * H * Lk > 0;
+  if (!has_q && !has_k) return FA_OK;
+  if (has_q && (!Q || !O || !dO || !lse || !dQ)) return FA_ERR_NULL;
+  if (has_k && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_bytes(in_dtype, B, H, Lq, Lk, d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
+
+  const size_t rows = (size_t)(B * H * Lq);
+  fa::BwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.lse = lse;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.Dvec = static_cast<float*>(workspace);
+  a.dQacc = in_dtype == FA_BF16 && workspace
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * sizeof(float), 256))
+                : nullptr;
+  a.BH = (int)(B * H);
+  a.Lq = (int)Lq;
+  a.Lk = (int)Lk;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  const hipError_t e = in_dtype == FA_BF16 ? fa::launch_bwd_bf16(a, stream) : fa::launch_bwd_f32(a, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal launchers behind the C ABI.  Arguments are already validated by
+// fa_api.hip; every launcher enqueues on `stream` and returns
+// hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* lse;
+  int BH, Lq, Lk, d;
+  float scale;
+  bool causal;
+  bool out_f32;
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dvec;   // [BH, Lq] row statistic (workspace)
+  float* dQacc;  // [BH, Lq, d] fp32 accumulator (workspace, bf16 path only)
+  int BH, Lq, Lk, d;
+  float scale;
+  bool causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
+
+// Work decomposition shared by validation and the launchers.
+constexpr int kFwdBf16RowsPerBlock = 128;
+constexpr int kBwdBf16KeysPerBlock = 128;
+constexpr int kF32RowsPerBlock = 64;
+
+}  // namespace fa

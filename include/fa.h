@@ -1,0 +1,144 @@
+/*
+ * fa.h - C ABI of libfa, exact blockwise scaled-dot-product attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every (batch b, head h) slice, with Q of shape
+ * [Lq, d], K and V of shape [Lk, d]:
+ *     S   = scale * Q K^T                       (Lq x Lk scores)
+ *     S_ij = -inf where causal and j > i        (mask; rows and keys are
+ *                                                aligned at index 0)
+ *     lse_i = log sum_j exp(S_ij)               (natural log)
+ *     O   = exp(S - lse) V
+ * This is the score matrix / softmax / value product of the "standard
+ * attention" that the blockwise method reproduces exactly ("How Flash
+ * Attention Improves Transformer Memory Efficiency ...", sections "Full
+ * Matrix Construction" and "Intermediate Tensor Storage"), computed instead
+ * tile by tile with an online softmax: a running max m, a running sum l and
+ * an unnormalised accumulator rescaled whenever the max grows, divided by l
+ * at the end (same page, section "The Three Running Statistics";
+ * "What Is FlashAttention?", section "What FlashAttention does instead").
+ * S and P are never written to device memory.
+ *
+ * The backward (loss <dO, O>) recomputes the probabilities from the saved
+ * lse and uses the row statistic D_i = sum_c dO_ic O_ic (annotated-code
+ * page, section "Backward Pass Efficiency"; glossary page "Flash
+ * Attention", section "How it works", on recomputing intermediates):
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * Conventions shared by every entry point:
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, L, d]
+ *              (d fastest, then L, then H, then B); lse and the D statistic
+ *              are dense [B, H, Lq] float.  Base pointers must be 16-byte
+ *              aligned.
+ *   Dtypes     FA_BF16 inputs compute on bf16 matrix cores with fp32
+ *              accumulation and fp32 softmax statistics; FA_F32 inputs
+ *              compute in fp32 throughout.
+ *   Ownership  Every pointer is a device pointer owned by the caller.  The
+ *              library never allocates or frees device memory and keeps no
+ *              state between calls; calls on different streams are
+ *              independent.
+ *   Execution  Work is enqueued on `stream` (NULL = the default stream) and
+ *              returns before it completes; there is no hidden synchronise.
+ *   Errors     Arguments are validated before any HIP call; an invalid call
+ *              returns a status and enqueues nothing.  A launch failure
+ *              reported by the HIP runtime returns FA_ERR_HIP.  No entry
+ *              point aborts or throws.
+ *   Empty      B, H or Lq equal to 0 is valid and does no work (the backward
+ *              with Lq = 0 still writes zero dK and dV).  Lk = 0 with Lq > 0
+ *              is FA_ERR_SHAPE: a softmax over no keys is undefined.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_API __attribute__((visibility("default")))
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,       /* negative size, Lk = 0 with Lq > 0, or a size too
+                             large for 32-bit per-slice offsets                 */
+  FA_ERR_UNSUPPORTED = 3, /* valid request the kernels do not implement (head
+                             dimension, dtype combination)                     */
+  FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned             */
+  FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
+  FA_ERR_ARG = 7          /* non-finite scale or an unknown enum value         */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_F32 = 0,
+  FA_BF16 = 1
+} fa_dtype;
+
+/*
+ * Forward: O and lse from Q, K, V.
+ *   in_dtype   dtype of Q, K, V.
+ *   out_dtype  dtype of O: equal to in_dtype, or FA_F32 with bf16 inputs
+ *              (the fp32 accumulator divided by l, not rounded to bf16).
+ *   B, H       batch and heads.  Lq, Lk: query and key lengths.  d: head
+ *              dimension; supported: 64 and 128.
+ *   Q          [B,H,Lq,d] in_dtype.   K, V: [B,H,Lk,d] in_dtype.
+ *   scale      score multiplier (callers usually pass 1/sqrt(d)); finite.
+ *   causal     nonzero: key j is hidden from query row i when j > i.
+ *   O          [B,H,Lq,d] out_dtype, written.
+ *   lse        [B,H,Lq] float, written: natural-log log-sum-exp of each
+ *              row's scaled, masked scores (saved for the backward).
+ * Per (b, h) slice, Lq*d and Lk*d times the element size must each stay
+ * below 2^31 bytes.
+ */
+FA_API fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 float scale, int causal,
+                 void* O, float* lse, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: the D statistic
+ * ([B,H,Lq] float) and, for bf16, an fp32 dQ accumulator ([B,H,Lq,d]).
+ * Linear in Lq; independent of the number of scores.  Returns 0 for sizes
+ * fa_bwd would reject.
+ */
+FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
+                              int64_t Lq, int64_t Lk, int64_t d);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, the forward's O and lse, and dO.
+ *   in_dtype   dtype of Q, K, V, O, dO, dQ, dK, dV (O and dO must be in
+ *              the input dtype; the fp32-output forward is a diagnostic).
+ *   lse        the forward's [B,H,Lq] output.
+ *   scale, causal  the values the forward was called with.
+ *   dQ         [B,H,Lq,d], dK, dV: [B,H,Lk,d], written.
+ *   workspace  device memory of at least fa_bwd_workspace_bytes(...) bytes,
+ *              16-byte aligned; its contents on entry do not matter and are
+ *              scratch afterwards.  Concurrent calls need separate
+ *              workspaces.
+ */
+FA_API fa_status fa_bwd(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse,
+                 float scale, int causal,
+                 void* dQ, void* dK, void* dV,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+FA_API const char* fa_status_str(fa_status s);
+
+/* Library version and target, e.g. "libfa 0.1.0 gfx950". */
+FA_API const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

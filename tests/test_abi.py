@@ -1,0 +1,125 @@
+"""The C ABI on the host: exported symbols, status codes of invalid calls
+(all rejected before any HIP call, so these run without a GPU), workspace
+sizing and the single HIP runtime.  Every call here is invalid or empty by
+construction; none reaches a kernel launch."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+from exact_io_aware_13_amd import _lib  # noqa: E402
+
+F32, BF16 = _lib.FA_F32, _lib.FA_BF16
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ARG = range(8)
+P = 0x10000  # a 16-byte-aligned stand-in address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _fwd(lib, in_dt=BF16, out_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, Q=P, K=P, V=P,
+         scale=0.125, causal=1, O=P, lse=P):
+    return lib.fa_fwd(in_dt, out_dt, B, H, Lq, Lk, d, Q, K, V, scale, causal, O, lse, None)
+
+
+def _bwd(lib, in_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125, causal=1,
+         ws=P, ws_bytes=None):
+    p = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dQ=P, dK=P, dV=P)
+    p.update(ptrs or {})
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(in_dt, B, H, Lq, Lk, d)
+    return lib.fa_bwd(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["O"], p["dO"], p["lse"],
+                      scale, causal, p["dQ"], p["dK"], p["dV"], ws, ws_bytes, None)
+
+
+def test_exports_match_header(lib):
+    declared = set(re.findall(r"FA_API\s+[\w\s\*]*?\b(fa_\w+)\s*\(", open(HEADER).read()))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"libfa does not export {name}"
+
+
+def test_exports_are_only_the_c_api():
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    text = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert text == set(_lib.EXPORTS), text
+
+
+def test_version(lib):
+    assert lib.fa_version().decode().startswith("libfa ")
+    assert "gfx950" in lib.fa_version().decode()
+
+
+def test_status_strings(lib):
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_str(code).decode().startswith(name)
+    assert lib.fa_status_str(99).decode() == "unknown fa_status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dt=5), ARG), (dict(out_dt=-1), ARG), (dict(scale=float("nan")), ARG),
+    (dict(scale=float("inf")), ARG),
+    (dict(B=-1), SHAPE), (dict(Lq=-3), SHAPE), (dict(d=0), SHAPE), (dict(Lk=0), SHAPE),
+    (dict(Lq=1 << 24), SHAPE), (dict(Lk=1 << 24), SHAPE), (dict(B=1 << 20, H=1 << 20), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=32), UNSUP), (dict(d=256), UNSUP),
+    (dict(in_dt=F32, out_dt=BF16), UNSUP),
+    (dict(Q=None), NULL), (dict(K=None), NULL), (dict(V=None), NULL), (dict(O=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(Q=P + 8), ALIGN), (dict(V=P + 2), ALIGN), (dict(O=P + 4), ALIGN), (dict(lse=P + 4), ALIGN),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(Lq=0), dict(Lq=0, Lk=0),
+                                dict(B=0, Lk=0)])
+def test_fwd_empty_is_ok_and_touches_nothing(lib, kw):
+    assert _fwd(lib, Q=None, K=None, V=None, O=None, lse=None, **kw) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dt=3), ARG), (dict(scale=float("nan")), ARG),
+    (dict(Lk=0), SHAPE), (dict(d=80), UNSUP),
+    (dict(ptrs=dict(dO=None)), NULL), (dict(ptrs=dict(lse=None)), NULL),
+    (dict(ptrs=dict(dV=None)), NULL), (dict(ptrs=dict(dQ=None)), NULL),
+    (dict(ptrs=dict(dK=P + 8)), ALIGN), (dict(ptrs=dict(O=P + 2)), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS), (dict(ws=P + 4), ALIGN),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_bwd_empty_is_ok(lib):
+    nul = {k: None for k in ("Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV")}
+    assert _bwd(lib, B=0, ptrs=nul, ws=None, ws_bytes=0) == OK
+
+
+def test_workspace_is_linear_in_length(lib):
+    mem = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_memory.json")))
+    L, L2 = mem["L"], mem["L_doubled"]
+    w1 = lib.fa_bwd_workspace_bytes(BF16, 1, 1, L, L, 128)
+    w2 = lib.fa_bwd_workspace_bytes(BF16, 1, 1, L2, L2, 128)
+    # D statistic plus fp32 dQ accumulator: exactly L*(4 + 4d) bytes here.
+    assert w1 == L * 4 + L * 128 * 4
+    assert w2 == 2 * w1                               # linear in L ...
+    assert mem["MiB_doubled"] == mem["growth_when_L_doubles"] * mem["MiB"]  # ... the scores grow 4x
+    assert mem["elements"] == L * L and mem["bytes"] == L * L * mem["bytes_per_element"]
+    assert w1 < mem["bytes"] / 10                     # far below one head's score matrix
+    assert lib.fa_bwd_workspace_bytes(F32, 1, 1, L, L, 128) == L * 4
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 1, L, L, 96) == 0
+    for L_ in (1024, 2048, 4096, 8192):
+        assert lib.fa_bwd_workspace_bytes(BF16, 1, 32, L_, L_, 128) == 32 * L_ * (4 + 512)
+
+
+def test_one_hip_runtime_is_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
