@@ -82,7 +82,18 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        x = torch.ones(64 * 2 ** 20, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the attention kernels run per device with no "
               f"cross-GPU exchange); --gpus {args.gpus} is not supported", file=sys.stderr)

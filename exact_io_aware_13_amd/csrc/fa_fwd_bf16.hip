@@ -1,62 +1,199 @@
 // Exact attention forward, bf16 inputs, fp32 accumulation, gfx950.
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, head) slice.  The
-// Q rows stay in registers for the whole key loop; K and V stream through
-// LDS one 64-key tile at a time (the next tile is fetched into registers
-// while the current one is multiplied), and an online softmax keeps a
-// running max m, a running sum l and an unnormalised output per row,
-// rescaling both by exp(m_old - m_new) when the max grows ("How Flash
-// Attention Improves Transformer Memory Efficiency ...", sections "Block-Wise
-// Processing Algorithm" and "The Three Running Statistics"; "What Is
-// FlashAttention?", section "What FlashAttention does instead").  Scores
-// and probabilities live only in registers.
+// One workgroup = 4 waves = 256 query rows of one (batch, head) slice; each
+// wave owns 64 rows as two 32-row blocks.  The Q rows stay in registers for
+// the whole key loop; K and V stream through LDS in 64-key tiles, and an
+// online softmax keeps a running max m, a running sum l and an unnormalised
+// output per row, rescaling both by exp(m_old - m_new) when the max moves
+// ("How Flash Attention Improves Transformer Memory Efficiency ...",
+// sections "Block-Wise Processing Algorithm" and "The Three Running
+// Statistics"; "What Is FlashAttention?", section "What FlashAttention does
+// instead").  Scores and probabilities live only in registers.
 //
-// Matrix-core orientation.  Each wave computes S^T = K Q^T for its 32 rows,
-// so in the 32x32 accumulator every lane owns ONE query row (column n = lane
-// % 32) and 16 of the tile's keys; the other 16 keys of that row sit in lane
-// ^ 32.  Row max and row sum are therefore in-lane plus one exchange between
-// the two wave halves.  The same register layout is then exactly the
-// B operand of O^T = V^T P^T: contraction order over keys is free, so the
-// keys are taken in the order the accumulator already holds them, and V^T is
-// read from a transposed copy of the V tile kept in LDS.  O^T's accumulator
-// again gives each lane one query row, so the rescale by exp(m_old - m_new)
-// is a per-lane scalar multiply.
+// Matrix-core orientation.  Each wave computes S^T = K Q^T for its rows, so
+// in the 32x32 accumulator every lane owns ONE query row (column n = lane %
+// 32) and 16 of a 32-key block; the other 16 keys of that row sit in lane ^
+// 32.  Row max and row sum are in-lane plus one exchange between the two
+// wave halves.  The same registers are the B operand of O^T = V^T P^T: the
+// contraction over keys is taken in the order the accumulator holds them,
+// and the A operand V^T comes from the row-major V tile through the
+// transposing LDS read (ds_read_b64_tr_b16: in each 16-lane group, lanes
+// 4j..4j+3 fetch four consecutive values of row j and lane u receives
+// element u of rows 0..3, i.e. four consecutive keys of one head-dim column).
+// O^T's accumulator again gives each lane one query row, so the rescale is a
+// per-lane scalar multiply.  Every K or V fragment read from LDS feeds the
+// products of both row blocks.
 //
-// Softmax arithmetic runs in base 2: scores are multiplied by
-// scale*log2(e), exponentials use the hardware exp2, and the stored lse is
-// converted back to natural log.  The running sum l adds the fp32
-// probabilities; the P.V product takes them rounded to bf16.  Summing the
-// unrounded values keeps lse within ~1e-6 of the exact log-normaliser even
-// for rows that see only a few keys (bf16 rounding of those few terms would
-// move ln l by up to ~2e-3).
+// Data movement.  K and V tiles go from HBM/L2 straight into LDS with
+// bounds-checked buffer loads (rows past the end of the slice read as zero),
+// no VGPR staging.  Each 16-byte chunk c of row r is stored at chunk
+// c ^ swz(r), so both the K reads (16 rows, one chunk each) and the
+// transposed V reads (4 rows x 32 bytes per 16 lanes) hit distinct banks.
+// K and V each use a 3-slot ring (one LDS array per slot, so the compiler
+// waits only for the load a read depends on); tile t's K is fetched two
+// iterations before the score product that needs it, its V two iterations
+// before the value product.
+//
+// Software pipeline.  Iteration j runs the score product of tile j+1 and the
+// value product of tile j-1 on the matrix cores while the vector ALUs run
+// the softmax of tile j.  The iteration body is scheduled by hand: 16 steps
+// of 4 matrix products, each LDS fragment read issued two steps ahead, the
+// softmax work items placed between the products.
+//
+// Softmax arithmetic runs in base 2: p = exp2(s * c - m) with c =
+// |scale| * log2(e) folded into one FMA (a negative scale is applied by
+// negating Q, which is exact in bf16); the row max is taken on the raw dot
+// products.  The reference max m is moved only when a row's max exceeds it
+// by more than 2^8: any reference gives the same O = acc / l and lse = m +
+// log2 l exactly, and keeping it fixed skips most rescales of the output
+// accumulator (probabilities then stay <= 2^8, far from overflow).  l sums
+// the fp32 probabilities; the value product takes them rounded to bf16.
+// Tiles that are fully masked for some rows (causal diagonal band) are still
+// multiplied; their probabilities are exactly 0.
 
 #include "fa_device.h"
 #include "fa_launch.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
 
 template <int D>
 struct FwdTile {
-  static constexpr int BR = 128;      // query rows per workgroup (32 per wave)
-  static constexpr int BC = 64;       // keys per tile
-  static constexpr int KS = D / 16;   // 16-deep steps over the head dimension
-  static constexpr int DB = D / 32;   // 32-wide blocks of the head dimension
-  static constexpr int KLD = D + 8;   // LDS pitch of K rows (bf16); +16 B keeps b128 reads conflict-free
-  static constexpr int VLD = BC + 4;  // LDS pitch of V^T rows (bf16); +8 B keeps b64 reads conflict-free
-  static constexpr int KCH = D / 8;   // 16-byte chunks per K/V row
-  static constexpr int K_ITEMS = BC * KCH / 256;  // K chunks fetched per thread
-  static constexpr int V_ITEMS = 16 * KCH;        // (4-key group, chunk) items of the V tile
+  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int RB = 2;                    // 32-row blocks per wave
+  static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
+  // Keys per tile: at d=128 a 32-key tile keeps the softmax working set
+  // (two score sets, two probability sets) inside the 256 VGPRs the vector
+  // ALUs address; d=64 has room for 64.
+  static constexpr int BC = D == 128 ? 32 : 64;
+  static constexpr int NKB = BC / 32;             // 32-key blocks per tile
+  static constexpr int KS = D / 16;               // 16-deep steps over the head dimension
+  static constexpr int DB = D / 32;               // 32-wide head-dim blocks
+  static constexpr int ROWB = D * 2;              // bytes per K/V row
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
+  static constexpr int RPK = 1024 / ROWB;         // rows per 1-KiB load instruction
+  static constexpr int LOADS = TILEB / 1024 / NW; // load instructions per wave per tile
+  static constexpr int NFRAG = NKB * KS;          // K fragments per tile (= V fragments)
+  static_assert(NFRAG == (BC / 16) * DB, "one K and one V fragment per step");
+  // Softmax work items per iteration (both row blocks): row-max partials over
+  // 8 scores, running statistics, probability pairs, running sums.
+  static constexpr int NMAXP = 2 * NKB;           // max partials per row block
+  static constexpr int NPAIR = 8 * NKB;           // probability pairs per row block
+  static constexpr int IT_STATS = RB * NMAXP;
+  static constexpr int IT_PAIRS = IT_STATS + RB;
+  static constexpr int IT_SUMS = IT_PAIRS + RB * NPAIR;
+  static constexpr int ITEMS = IT_SUMS + RB;
+  // Step s of the NFRAG steps runs items [item_begin(s), item_end(s)): all max
+  // partials in step 0, the statistics and two pairs in step 1, then three
+  // items per step.
+  static constexpr int item_begin(int s) {
+    const int b = s == 0 ? 0 : s == 1 ? IT_STATS : IT_PAIRS + 2 + 3 * (s - 2);
+    return b < ITEMS ? b : ITEMS;
+  }
+  static constexpr int item_end(int s) { return s == NFRAG - 1 ? ITEMS : item_begin(s + 1); }
 };
 
+// Chunk swizzle: bijective on the row index mod 16 (d=128) or on row/2 mod 8
+// (d=64), and spreads the 4 rows of a transposed read over all banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// s_waitcnt vmcnt(N) leaving expcnt and lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier that leaves buffer loads in flight: completes this wave's
+// LDS reads (lgkmcnt(0)), then s_barrier.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Calls f(IC<B>{}), ..., f(IC<E-1>{}): loop bodies with compile-time indices,
+// so register arrays are never indexed at run time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Row max / row sum across the two wave halves (lanes l and l ^ 32 hold the
+// two halves of one query row).  v_permlane32_swap exchanges the upper 32
+// lanes of its first operand with the lower 32 lanes of its second; applied
+// to two copies of x, every lane ends up with its own value in one register
+// and its partner's in the other.  Issued as a single VALU instruction in
+// asm: given identical operands, the compiler otherwise treats the two
+// results of the builtin as equal and drops one.
+__device__ __forceinline__ void halves_pair(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  // The nops give the wait states a VALU write needs before the swap reads
+  // it (the compiler cannot see hazards inside asm).
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return a + b;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
-    int BH, int Lq, int Lk, int n_qt, float scale_log2) {
+    int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[T::BC * T::KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * T::VLD];
+  __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V1[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V2[T::TILEB];
+  auto kslot = [&](auto I) __attribute__((always_inline)) -> char* {
+    if constexpr (decltype(I)::value == 0) return K0;
+    else if constexpr (decltype(I)::value == 1) return K1;
+    else return K2;
+  };
+  auto vslot = [&](auto I) __attribute__((always_inline)) -> char* {
+    if constexpr (decltype(I)::value == 0) return V0;
+    else if constexpr (decltype(I)::value == 1) return V1;
+    else return V2;
+  };
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -67,6 +204,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   int qt = blockIdx.x / BH;
   if (CAUSAL) qt = n_qt - 1 - qt;
   const int q0 = qt * T::BR;
+  const int qw0 = q0 + 64 * w;  // this wave's first row
 
   const size_t qoff = (size_t)bh * Lq * D;
   const size_t koff = (size_t)bh * Lk * D;
@@ -74,185 +212,381 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const auto rk = make_rsrc(K + koff, (uint32_t)Lk * D * 2);
   const auto rv = make_rsrc(V + koff, (uint32_t)Lk * D * 2);
 
-  // This lane's query row; its Q values are the B operand of S^T = K Q^T.
-  const int qg = q0 + w * 32 + n;
-  bf16x8 qf[T::KS];
-#pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks)
-    qf[ks] = as_bf16x8(load16(rq, (uint32_t)(qg * D + ks * 16 + h * 8) * 2));
-
-  f32x16 oacc[T::DB];
-#pragma unroll
-  for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
   int nkt = (Lk + T::BC - 1) / T::BC;
   if (CAUSAL) nkt = min(nkt, (q0 + T::BR - 1) / T::BC + 1);
 
-  u32x4 kreg[T::K_ITEMS];
-  u32x4 vreg[4];
-  auto fetch = [&](int kt) {
+  // ---- tile fetch: each wave moves LOADS KiB of the K (or V) tile ----------
+  // Lane l of load i writes LDS bytes [16 l, 16 l + 16) of KiB (w*LOADS + i)
+  // of the slot; it fetches the logical chunk that the swizzle puts there.
+  int fetch_off[T::LOADS];
 #pragma unroll
-    for (int i = 0; i < T::K_ITEMS; ++i) {
-      const int it = tid + 256 * i, row = it / T::KCH, ch = it % T::KCH;
-      kreg[i] = load16(rk, (uint32_t)((kt * T::BC + row) * D + ch * 8) * 2);
-    }
-    if (tid < T::V_ITEMS) {
-      const int kg = tid % 16, ch = tid / 16;
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int row = (w * T::LOADS + i) * T::RPK + lane / T::CPR;
+    const int chunk = (lane % T::CPR) ^ swz<D>(row);
+    fetch_off[i] = (row * D + chunk * 8) * 2;
+  }
+  auto fetch = [&](const __amdgpu_buffer_rsrc_t& r, int tile, char* slot)
+                   __attribute__((always_inline)) {
+    // Tiles past the last one re-fetch the last tile into a free slot, which
+    // keeps the number of loads in flight the same every iteration.
+    const int t = min(tile, nkt - 1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[r] = load16(rv, (uint32_t)((kt * T::BC + 4 * kg + r) * D + ch * 8) * 2);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::K_ITEMS; ++i) {
-      const int it = tid + 256 * i, row = it / T::KCH, ch = it % T::KCH;
-      *reinterpret_cast<u32x4*>(&Ks[row * T::KLD + ch * 8]) = kreg[i];
-    }
-    if (tid < T::V_ITEMS) {
-      // Four keys x eight head-dim values -> eight rows of V^T, four keys each.
-      const int kg = tid % 16, ch = tid / 16;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 ev, od;
-        ev.x = (vreg[0][a] & 0xffffu) | (vreg[1][a] << 16);
-        ev.y = (vreg[2][a] & 0xffffu) | (vreg[3][a] << 16);
-        od.x = (vreg[0][a] >> 16) | (vreg[1][a] & 0xffff0000u);
-        od.y = (vreg[2][a] >> 16) | (vreg[3][a] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(&Vt[(ch * 8 + 2 * a) * T::VLD + 4 * kg]) = ev;
-        *reinterpret_cast<u32x2*>(&Vt[(ch * 8 + 2 * a + 1) * T::VLD + 4 * kg]) = od;
-      }
-    }
+    for (int i = 0; i < T::LOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void*)(slot + (w * T::LOADS + i) * 1024), 16,
+          (uint32_t)(t * T::TILEB + fetch_off[i]), 0, 0, 0);
   };
 
-  fetch(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();  // all waves are done reading the previous tile
-    stage();
-    __syncthreads();
-    if (kt + 1 < nkt) fetch(kt + 1);
+  // ---- per-lane LDS read offsets (slot-relative) -----------------------------
+  // K fragment f (key block f%NKB, step f/NKB): row (f%NKB)*32 + n, chunk
+  // 2(f/NKB) + h.
+  const int ksw = swz<D>(n);
+  int koffs[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) koffs[ks] = n * T::ROWB + (((2 * ks + h) ^ ksw) << 4);
+  // V^T fragment f (key step f/DB, head-dim block f%DB): two transposed reads
+  // of rows 16*step + 4h + j (+8), columns 32db + 16(g%2) + 4t .. +3.
+  const int g = lane >> 4, u = lane & 15, j4 = u >> 2, t4 = u & 3;
+  int voffs[2][T::DB];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = 8 * half + 4 * h + j4;
+    const int sw = swz<D>(row);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const int chunk = 4 * db + 2 * (g & 1) + (t4 >> 1);
+      voffs[half][db] = row * T::ROWB + ((chunk ^ sw) << 4) + 8 * (t4 & 1);
+    }
+  }
+  auto kread = [&](const char* kb, int f) __attribute__((always_inline)) {
+    return lds_read16(kb, (f % T::NKB) * 32 * T::ROWB + koffs[f / T::NKB]);
+  };
+  auto vread = [&](const char* vb, int f) __attribute__((always_inline)) {
+    const int step = f / T::DB, db = f % T::DB;
+    const u32x2 lo = lds_read_tr(vb, step * 16 * T::ROWB + voffs[0][db]);
+    const u32x2 hi = lds_read_tr(vb, step * 16 * T::ROWB + voffs[1][db]);
+    u32x4 a;
+    a.x = lo.x;
+    a.y = lo.y;
+    a.z = hi.x;
+    a.w = hi.y;
+    return a;
+  };
 
-    // S^T for 2 blocks of 32 keys: lane owns query qg, register r of block kb
-    // holds key kt*64 + kb*32 + 8*(r/4) + 4*h + r%4.
-    f32x16 s[2];
+  // ---- Q fragments (B operands of S^T = K Q^T), one set per row block ------
+  bf16x8 qf[T::RB][T::KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+  for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&Ks[(kb * 32 + n) * T::KLD + ks * 16 + h * 8]);
-        s[kb] = mma(as_bf16x8(a), qf[ks], s[kb]);
-      }
+    for (int ks = 0; ks < T::KS; ++ks) {
+      u32x4 v = load16(rq, (uint32_t)((qw0 + 32 * rb + n) * D + ks * 16 + h * 8) * 2);
+      v ^= qsign;  // negative scale: negate Q (sign flip of every bf16)
+      qf[rb][ks] = as_bf16x8(v);
     }
 
-    const int key0 = kt * T::BC;
-    const bool need_mask = (key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > q0 + w * 32);
-    float mx = -INFINITY;
+  f32x16 oacc[T::RB][T::DB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+  float m[T::RB] = {-INFINITY, -INFINITY}, l[T::RB] = {0.f, 0.f};
+
+  // Pipeline registers: raw scores of the current and next tile, packed bf16
+  // probabilities of the previous and current tile.  Defined up front: the
+  // first and last iterations leave some of them unwritten.
+  f32x16 sA[T::RB][T::NKB], sB[T::RB][T::NKB];
+  unsigned pA[T::RB][T::NKB][8], pB[T::RB][T::NKB][8];
+#pragma unroll
+  for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < T::NKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float t = s[kb][r] * scale_log2;
-        if (need_mask) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= Lk || (CAUSAL && key > qg)) t = -INFINITY;
+        sA[rb][kb][r] = 0.f;
+        sB[rb][kb][r] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pA[rb][kb][i] = 0u;
+        pB[rb][kb][i] = 0u;
+      }
+    }
+
+  // Whole-tile score product (prologue only; iterations interleave it).
+  auto score_tile = [&](const char* kb, f32x16 (&s)[T::RB][T::NKB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < T::NFRAG; ++f) {
+      const bf16x8 a = as_bf16x8(kread(kb, f));
+#pragma unroll
+      for (int rb = 0; rb < T::RB; ++rb) {
+        if (f < T::NKB) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          s[rb][f % T::NKB] = mma(a, qf[rb][f / T::NKB], z);
+        } else {
+          s[rb][f % T::NKB] = mma(a, qf[rb][f / T::NKB], s[rb][f % T::NKB]);
         }
-        s[kb][r] = t;
-        mx = fmaxf(mx, t);
       }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m, mx);
-    // A row whose keys so far are all masked keeps m = -inf; exponentiate
-    // against 0 then, so masked entries give exactly 0 and nothing is NaN.
-    const float base = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - base);
-    m = m_new;
+    }
+  };
+  // Whole-tile value product (epilogue only).
+  auto value_tile = [&](const char* vb, const unsigned (&pk)[T::RB][T::NKB][8])
+                        __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < T::NFRAG; ++f) {
+      const bf16x8 a = as_bf16x8(vread(vb, f));
+      const int step = f / T::DB, db = f % T::DB, kb = step >> 1, hf = step & 1;
+#pragma unroll
+      for (int rb = 0; rb < T::RB; ++rb) {
+        u32x4 bp;
+        bp.x = pk[rb][kb][hf * 4 + 0];
+        bp.y = pk[rb][kb][hf * 4 + 1];
+        bp.z = pk[rb][kb][hf * 4 + 2];
+        bp.w = pk[rb][kb][hf * 4 + 3];
+        oacc[rb][db] = mma(a, as_bf16x8(bp), oacc[rb][db]);
+      }
+    }
+  };
 
-    unsigned pk[2][8];
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p0 = fast_exp2(s[kb][2 * j] - base), p1 = fast_exp2(s[kb][2 * j + 1] - base);
-        pk[kb][j] = pack_bf16x2(p0, p1);
-        rs += p0 + p1;
-      }
-    l = alpha * l + rs;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+  // One pipelined iteration j.  R = j mod 6 fixes the ring slots and which
+  // register set is current; FIRST (j = 0) has no previous value product.
+  auto iter = [&](auto Rc, auto FIRSTc, int j, f32x16 (&s_cur)[T::RB][T::NKB],
+                  f32x16 (&s_next)[T::RB][T::NKB], const unsigned (&pk_prev)[T::RB][T::NKB][8],
+                  unsigned (&pk_cur)[T::RB][T::NKB][8]) __attribute__((always_inline)) {
+    constexpr int R = decltype(Rc)::value;
+    constexpr bool FIRST = decltype(FIRSTc)::value;
+    const char* kb = kslot(IC<(R + 1) % 3>{});
+    const char* vb = vslot(IC<(R + 2) % 3>{});
 
-    // O^T += V^T P^T in 4 steps of 16 keys.  Step ks2 uses registers
-    // 8*(ks2%2) .. +7 of score block ks2/2; slot i of half h is key
-    // ks2*16 + 8*(i/4) + 4*h + i%4, which V^T supplies as two 4-key runs.
+    block_barrier();  // every wave is done with the slots refilled below
+    fetch(rk, j + 3, kslot(IC<R % 3>{}));
+    fetch(rv, j + 1, vslot(IC<(R + 1) % 3>{}));
+    wait_vm<4 * T::LOADS>();  // K[j+1] and V[j-1] landed: only the 2 newest iterations in flight
+    block_barrier();
+
+    // Mask tile j where it crosses the causal diagonal or the end of the keys.
+    const int key0 = j * T::BC;
+    if ((key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > qw0)) {
+      // Register r of key block kb2 holds key key0 + 4h + (kb2*32 + 8(r/4) + r%4);
+      // it is visible iff that constant offset is <= lim.  The sign of
+      // (lim - offset) selects -inf without compares.
+      static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
+        constexpr int rb = decltype(RBc)::value;
+        const int qrow = qw0 + 32 * rb + n;
+        const int last = CAUSAL ? min(Lk - 1, qrow) : Lk - 1;
+        const int lim = last - key0 - 4 * h;
+        static_for<0, 16 * T::NKB>([&](auto Ec) __attribute__((always_inline)) {
+          constexpr int e = decltype(Ec)::value, kb2 = e >> 4, r = e & 15;
+          constexpr int off = kb2 * 32 + 8 * (r >> 2) + (r & 3);
+          const unsigned hide = (unsigned)((lim - off) >> 31);
+          // Copy the element first: bit_cast of a vector-element lvalue reads
+          // element 0 regardless of the index.
+          const float sv = s_cur[rb][kb2][r];
+          const unsigned bits = __builtin_bit_cast(unsigned, sv);
+          s_cur[rb][kb2][r] = __builtin_bit_cast(float, (hide & 0xff800000u) | (~hide & bits));
+        });
+      });
+    }
+
+    float mxp[T::RB][T::NMAXP], rs[T::RB][4], alpha[T::RB], base[T::RB];
 #pragma unroll
-    for (int ks2 = 0; ks2 < T::BC / 16; ++ks2) {
-      const int kb = ks2 >> 1, hf = ks2 & 1;
-      u32x4 bp;
-      bp.x = pk[kb][hf * 4 + 0];
-      bp.y = pk[kb][hf * 4 + 1];
-      bp.z = pk[kb][hf * 4 + 2];
-      bp.w = pk[kb][hf * 4 + 3];
+    for (int rb = 0; rb < T::RB; ++rb) {
+      alpha[rb] = 1.f;
+      base[rb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int dd = db * 32 + n;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[dd * T::VLD + ks2 * 16 + 4 * h]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[dd * T::VLD + ks2 * 16 + 8 + 4 * h]);
-        u32x4 av;
-        av.x = lo.x;
-        av.y = lo.y;
-        av.z = hi.x;
-        av.w = hi.y;
-        oacc[db] = mma(as_bf16x8(av), as_bf16x8(bp), oacc[db]);
+      for (int i = 0; i < 4; ++i) rs[rb][i] = 0.f;
+    }
+    auto item = [&](auto ITc) __attribute__((always_inline)) {
+      constexpr int it = decltype(ITc)::value;
+      if constexpr (it < T::IT_STATS) {  // row-max partial over 8 scores
+        constexpr int rb = it / T::NMAXP, k = it % T::NMAXP, kb2 = k >> 1, r0 = (k & 1) * 8;
+        const f32x16& x = s_cur[rb][kb2];
+        mxp[rb][k] = fmaxf(fmaxf(fmaxf(x[r0], x[r0 + 1]), fmaxf(x[r0 + 2], x[r0 + 3])),
+                           fmaxf(fmaxf(x[r0 + 4], x[r0 + 5]), fmaxf(x[r0 + 6], x[r0 + 7])));
+      } else if constexpr (it < T::IT_PAIRS) {  // running statistics
+        constexpr int rb = it - T::IT_STATS;
+        float mx = mxp[rb][0];
+        static_for<1, T::NMAXP>([&](auto Kc) __attribute__((always_inline)) {
+          mx = fmaxf(mx, mxp[rb][decltype(Kc)::value]);
+        });
+        mx = halves_max(mx);
+        const float mt = mx * c;  // -inf stays -inf (c > 0)
+        const float m_new = (mt > m[rb] + 8.f) ? mt : m[rb];
+        alpha[rb] = (m_new == m[rb]) ? 1.f : fast_exp2(m[rb] - m_new);
+        m[rb] = m_new;
+        base[rb] = m_new;
+      } else if constexpr (it < T::IT_SUMS) {  // one pair of probabilities
+        constexpr int pi = it - T::IT_PAIRS, rb = pi & 1, p = pi >> 1, kb2 = p >> 3, jj = p & 7;
+        const float p0 = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][2 * jj], c, -base[rb]));
+        const float p1 = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][2 * jj + 1], c, -base[rb]));
+        pk_cur[rb][kb2][jj] = pack_bf16x2(p0, p1);
+        rs[rb][p & 3] += p0 + p1;
+      } else {  // running sum
+        constexpr int rb = it - T::IT_SUMS;
+        l[rb] = alpha[rb] * l[rb] + ((rs[rb][0] + rs[rb][1]) + (rs[rb][2] + rs[rb][3]));
       }
+    };
+    // Runs the softmax item with number IT if it belongs to the range [B, E).
+    auto item_if = [&](auto ITc, auto Bc, auto Ec) __attribute__((always_inline)) {
+      constexpr int it = decltype(ITc)::value;
+      if constexpr (it >= decltype(Bc)::value && it < decltype(Ec)::value) item(IC<it>{});
+    };
+
+    // 16 steps: score product of K fragment i for both row blocks, value
+    // product of V fragment i for both row blocks, softmax items in between.
+    u32x4 ka[T::NFRAG], va[T::NFRAG];
+    ka[0] = kread(kb, 0);
+    ka[1] = kread(kb, 1);
+    if constexpr (!FIRST) {
+      va[0] = vread(vb, 0);
+      va[1] = vread(vb, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, T::NFRAG>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      constexpr int ib = T::item_begin(i), ie = T::item_end(i);
+      if constexpr (i + 2 < T::NFRAG) {
+        ka[i + 2] = kread(kb, i + 2);
+        if constexpr (!FIRST) va[i + 2] = vread(vb, i + 2);
+      }
+      static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
+        constexpr int rb = decltype(RBc)::value;
+        constexpr int kb2 = i % T::NKB, ks = i / T::NKB;
+        if constexpr (i < T::NKB) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          s_next[rb][kb2] = mma(as_bf16x8(ka[i]), qf[rb][ks], z);
+        } else {
+          s_next[rb][kb2] = mma(as_bf16x8(ka[i]), qf[rb][ks], s_next[rb][kb2]);
+        }
+        item_if(IC<ib + rb>{}, IC<ib>{}, IC<ie>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (!FIRST) {
+        constexpr int step = i / T::DB, db = i % T::DB, kb2 = step >> 1, hf = step & 1;
+        static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
+          constexpr int rb = decltype(RBc)::value;
+          u32x4 bp;
+          bp.x = pk_prev[rb][kb2][hf * 4 + 0];
+          bp.y = pk_prev[rb][kb2][hf * 4 + 1];
+          bp.z = pk_prev[rb][kb2][hf * 4 + 2];
+          bp.w = pk_prev[rb][kb2][hf * 4 + 3];
+          oacc[rb][db] = mma(as_bf16x8(va[i]), as_bf16x8(bp), oacc[rb][db]);
+          item_if(IC<ib + 2 + rb>{}, IC<ib>{}, IC<ie>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+        item_if(IC<ib + 2>{}, IC<ib>{}, IC<ie>{});
+        item_if(IC<ib + 3>{}, IC<ib>{}, IC<ie>{});
+      }
+      // Items beyond four in this step.
+      static_for<ib + 4, (ie > ib + 4 ? ie : ib + 4)>(
+          [&](auto ITc) __attribute__((always_inline)) { item(ITc); });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // Rescale after P(j-1)V(j-1) is in, before P(j)V(j) is added.
+    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+      for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha[rb];
+    }
+  };
+
+  // ---- prologue ---------------------------------------------------------------
+  // Fetch order K0, K1, K2, V0; iteration j then fetches K[j+3] and V[j+1].
+  fetch(rk, 0, K0);
+  fetch(rk, 1, K1);
+  fetch(rk, 2, K2);
+  fetch(rv, 0, V0);
+  wait_vm<3 * T::LOADS>();  // K0 landed
+  block_barrier();
+  score_tile(K0, sA);
+
+  iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB);
+  // Six iterations per trip (j = 1..6 mod 6) as one straight-line chain, so
+  // ring slots and register roles are compile-time in every body.
+  for (int j = 1; j < nkt; j += 6) {
+    iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA);
+    if (j + 1 >= nkt) break;
+    iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB);
+    if (j + 2 >= nkt) break;
+    iter(IC<3>{}, std::false_type{}, j + 2, sB, sA, pB, pA);
+    if (j + 3 >= nkt) break;
+    iter(IC<4>{}, std::false_type{}, j + 3, sA, sB, pA, pB);
+    if (j + 4 >= nkt) break;
+    iter(IC<5>{}, std::false_type{}, j + 4, sB, sA, pB, pA);
+    if (j + 5 >= nkt) break;
+    iter(IC<0>{}, std::false_type{}, j + 5, sA, sB, pA, pB);
+  }
+
+  // Value product of the last tile: P(nkt-1) is in pB when nkt-1 is even.
+  wait_vm<0>();
+  block_barrier();
+  {
+    const unsigned(&plast)[T::RB][T::NKB][8] = ((nkt - 1) & 1) ? pA : pB;
+    switch ((nkt - 1) % 3) {
+      case 0: value_tile(V0, plast); break;
+      case 1: value_tile(V1, plast); break;
+      default: value_tile(V2, plast); break;
     }
   }
 
-  // Epilogue: O = accumulator / l, lse = (m + log2 l) * ln 2.
-  const float lt = l + swap_halves(l);
-  const float inv = 1.f / lt;
-  if (OUT_F32) {
-    const auto ro = make_rsrc(static_cast<float*>(O) + qoff, (uint32_t)Lq * D * 4);
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) * ln 2 ---------------------
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+  for (int rb = 0; rb < T::RB; ++rb) {
+    const int qg = qw0 + 32 * rb + n;
+    const float lt = halves_sum(l[rb]);
+    const float inv = 1.f / lt;
+    if (OUT_F32) {
+      const auto ro = make_rsrc(static_cast<float*>(O) + qoff, (uint32_t)Lq * D * 4);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x4 v;
-        v.x = __builtin_bit_cast(unsigned, oacc[db][4 * g + 0] * inv);
-        v.y = __builtin_bit_cast(unsigned, oacc[db][4 * g + 1] * inv);
-        v.z = __builtin_bit_cast(unsigned, oacc[db][4 * g + 2] * inv);
-        v.w = __builtin_bit_cast(unsigned, oacc[db][4 * g + 3] * inv);
-        store16(ro, (uint32_t)(qg * D + db * 32 + 8 * g + 4 * h) * 4, v);
-      }
-  } else {
-    const auto ro = make_rsrc(static_cast<uint16_t*>(O) + qoff, (uint32_t)Lq * D * 2);
+      for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x4 v;
+          v.x = __builtin_bit_cast(unsigned, oacc[rb][db][4 * g4 + 0] * inv);
+          v.y = __builtin_bit_cast(unsigned, oacc[rb][db][4 * g4 + 1] * inv);
+          v.z = __builtin_bit_cast(unsigned, oacc[rb][db][4 * g4 + 2] * inv);
+          v.w = __builtin_bit_cast(unsigned, oacc[rb][db][4 * g4 + 3] * inv);
+          store16(ro, (uint32_t)(qg * D + db * 32 + 8 * g4 + 4 * h) * 4, v);
+        }
+    } else {
+      const auto ro = make_rsrc(static_cast<uint16_t*>(O) + qoff, (uint32_t)Lq * D * 2);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 v;
-        v.x = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        v.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        store8(ro, (uint32_t)(qg * D + db * 32 + 8 * g + 4 * h) * 2, v);
-      }
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 v;
+          v.x = pack_bf16x2(oacc[rb][db][4 * g4 + 0] * inv, oacc[rb][db][4 * g4 + 1] * inv);
+          v.y = pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv);
+          store8(ro, (uint32_t)(qg * D + db * 32 + 8 * g4 + 4 * h) * 2, v);
+        }
+    }
+    if (h == 0 && qg < Lq) LSE[(size_t)bh * Lq + qg] = (m[rb] + __log2f(lt)) * kLn2;
   }
-  if (h == 0 && qg < Lq) LSE[(size_t)bh * Lq + qg] = (m + __log2f(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  const int n_qt = (a.Lq + FwdTile<D>::BR - 1) / FwdTile<D>::BR;
+  using T = FwdTile<D>;
+  const int n_qt = (a.Lq + T::BR - 1) / T::BR;
   const dim3 grid((unsigned)(n_qt * a.BH));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32>), grid, dim3(256), 0, stream,
+  // c = |scale| log2(e), kept > 0 so masked (-inf) scores give exactly 0; a
+  // zero scale uses a tiny c, which gives probabilities of exactly 1.0f.
+  float c = fabsf(a.scale) * kLog2e;
+  if (c < 1e-30f) c = 1e-30f;
+  const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32>), grid, dim3(64 * T::NW), 0, stream,
                      static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-                     static_cast<const uint16_t*>(a.V), a.O, a.lse, a.BH, a.Lq, a.Lk, n_qt,
-                     a.scale * kLog2e);
+                     static_cast<const uint16_t*>(a.V), a.O, a.lse, a.BH, a.Lq, a.Lk, n_qt, c,
+                     qsign);
   return hipGetLastError();
 }
 

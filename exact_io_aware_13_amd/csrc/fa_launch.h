@@ -43,7 +43,7 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
 
 // Work decomposition shared by validation and the launchers.
-constexpr int kFwdBf16RowsPerBlock = 128;
+constexpr int kFwdBf16RowsPerBlock = 256;
 constexpr int kBwdBf16KeysPerBlock = 128;
 constexpr int kF32RowsPerBlock = 64;
 
