@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
     float* __restrict__ dQacc, int64_t rows) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;    // rows per workgroup
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
+  const int64_t row = (int64_t)wg_id() * RPB + wi_id() / LPR;
+  const int c = wi_id() % LPR;
   float acc = 0.f;
   if (row < rows) {
     const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * D + c * 8);
@@ -91,10 +91,13 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float lse_s[T::BQ];
   __shared__ __attribute__((aligned(16))) float dd_s[T::BQ];
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.x % BH;
-  const int k0 = (blockIdx.x / BH) * T::BK;
+  const int tid = wi_id();
+  // The wave index is the same on every lane; readfirstlane tells the
+  // compiler so, which keeps everything derived from it in scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int bh = wg_id() % BH;
+  const int k0 = (wg_id() / BH) * T::BK;
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + n;
 
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
                                                          uint16_t* __restrict__ dQ, float scale,
                                                          int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = (int64_t)wg_id() * 256 + wi_id();
   if (i >= n8) return;
   const f32x4 a = *reinterpret_cast<const f32x4*>(acc + 8 * i);
   const f32x4 b = *reinterpret_cast<const f32x4*>(acc + 8 * i + 4);

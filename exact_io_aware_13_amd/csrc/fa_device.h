@@ -16,6 +16,14 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
+// Workgroup and work-item index read straight from the hardware registers.
+// The blockIdx/threadIdx accessors go through small library functions that
+// the inliner may leave out of line in a large kernel; their results then
+// count as per-lane values, and every buffer descriptor derived from the
+// workgroup index turns into a per-lane loop around each buffer access.
+__device__ __forceinline__ int wg_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int wi_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -30,9 +30,9 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
                                                         int Lk, int n_qt, float scale_log2) {
   __shared__ float Kl[kTile][D];
   __shared__ float Vl[kTile][D];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x % BH;
-  const int qt = blockIdx.x / BH;
+  const int tid = wi_id();
+  const int bh = wg_id() % BH;
+  const int qt = wg_id() / BH;
   const int qi = qt * kRows + tid;
   const bool valid = qi < Lq;
   const float* q = Q + ((size_t)bh * Lq + (valid ? qi : 0)) * D;
@@ -101,7 +101,7 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restrict__ O,
                                                           const float* __restrict__ dO,
                                                           float* __restrict__ Dvec, int64_t rows) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = (int64_t)wg_id() * 256 + wi_id();
   if (r >= rows) return;
   float acc = 0.f;
   for (int c = 0; c < D; ++c) acc = fmaf(O[r * D + c], dO[r * D + c], acc);
@@ -120,9 +120,9 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
   __shared__ float Ll[kTile], Dl[kTile];
   __shared__ float accK[D][kRows];
   __shared__ float accV[D][kRows];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x % BH;
-  const int kblk = blockIdx.x / BH;
+  const int tid = wi_id();
+  const int bh = wg_id() % BH;
+  const int kblk = wg_id() / BH;
   const int kj = kblk * kRows + tid;
   const bool valid = kj < Lk;
   const float* kp = K + ((size_t)bh * Lk + (valid ? kj : 0)) * D;
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
   __shared__ float Kl[kTile][D];
   __shared__ float Vl[kTile][D];
   __shared__ float accQ[D][kRows];
-  const int tid = threadIdx.x;
-  const int bh = blockIdx.x % BH;
-  const int qt = blockIdx.x / BH;
+  const int tid = wi_id();
+  const int bh = wg_id() % BH;
+  const int qt = wg_id() / BH;
   const int qi = qt * kRows + tid;
   const bool valid = qi < Lq;
   const size_t row = (size_t)bh * Lq + (valid ? qi : 0);

@@ -78,22 +78,18 @@ struct FwdTile {
   static constexpr int LOADS = TILEB / 1024 / NW; // load instructions per wave per tile
   static constexpr int NFRAG = NKB * KS;          // K fragments per tile (= V fragments)
   static_assert(NFRAG == (BC / 16) * DB, "one K and one V fragment per step");
-  // Softmax work items per iteration (both row blocks): row-max partials over
-  // 8 scores, running statistics, probability pairs, running sums.
-  static constexpr int NMAXP = 2 * NKB;           // max partials per row block
-  static constexpr int NPAIR = 8 * NKB;           // probability pairs per row block
-  static constexpr int IT_STATS = RB * NMAXP;
-  static constexpr int IT_PAIRS = IT_STATS + RB;
-  static constexpr int IT_SUMS = IT_PAIRS + RB * NPAIR;
-  static constexpr int ITEMS = IT_SUMS + RB;
-  // Step s of the NFRAG steps runs items [item_begin(s), item_end(s)): all max
-  // partials in step 0, the statistics and two pairs in step 1, then three
-  // items per step.
-  static constexpr int item_begin(int s) {
-    const int b = s == 0 ? 0 : s == 1 ? IT_STATS : IT_PAIRS + 2 + 3 * (s - 2);
-    return b < ITEMS ? b : ITEMS;
-  }
-  static constexpr int item_end(int s) { return s == NFRAG - 1 ? ITEMS : item_begin(s + 1); }
+  // Softmax slot program (both row blocks): row-max chains, running
+  // statistics, 4-probability groups in three stages, running sums.
+  static constexpr int NMAXP = 2 * NKB;           // max chains per row block (8 scores each)
+  static constexpr int NGROUP = RB * 4 * NKB;     // 4-probability groups per iteration
+  static constexpr int SL_STATS = RB * NMAXP;
+  static constexpr int SL_GROUPS = SL_STATS + RB;
+  static constexpr int SL_SUMS = SL_GROUPS + 3 * NGROUP;
+  static constexpr int NPROG = SL_SUMS + RB;      // program slots
+  static constexpr int NPHYS = 4 * NFRAG;         // matrix-product slots per iteration
+  // Program slots run after physical slot p: [prog_begin(p), prog_begin(p+1)),
+  // an even spread of the program over the products.
+  static constexpr int prog_begin(int p) { return (p * NPROG + NPHYS - 1) / NPHYS; }
 };
 
 // Chunk swizzle: bijective on the row index mod 16 (d=128) or on row/2 mod 8
@@ -136,6 +132,13 @@ __device__ __forceinline__ void block_barrier() {
 
 template <int N>
 using IC = std::integral_constant<int, N>;
+
+// Pins a value at this point of the instruction stream: the empty asm
+// "modifies" it, so it must be computed before and cannot be sunk past it.
+// Keeps the hand-placed softmax work between the matrix products it is meant
+// to overlap (scheduling barriers alone do not stop code sinking).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 
 // Calls f(IC<B>{}), ..., f(IC<E-1>{}): loop bodies with compile-time indices,
 // so register arrays are never indexed at run time.
@@ -195,13 +198,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     else return V2;
   };
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int tid = wi_id();
+  // The wave index is the same on every lane; readfirstlane tells the
+  // compiler so, which keeps everything derived from it in scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, n = lane & 31, h = lane >> 5;
 
   // Consecutive workgroups take the same query tile of different slices; for
   // causal masks the tiles with the most visible keys are dispatched first.
-  const int bh = blockIdx.x % BH;
-  int qt = blockIdx.x / BH;
+  const int bh = wg_id() % BH;
+  int qt = wg_id() / BH;
   if (CAUSAL) qt = n_qt - 1 - qt;
   const int q0 = qt * T::BR;
   const int qw0 = q0 + 64 * w;  // this wave's first row
@@ -392,6 +398,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     }
 
     float mxp[T::RB][T::NMAXP], rs[T::RB][4], alpha[T::RB], base[T::RB];
+    float xg[T::NGROUP][4];  // probability groups in flight between stages
 #pragma unroll
     for (int rb = 0; rb < T::RB; ++rb) {
       alpha[rb] = 1.f;
@@ -399,15 +406,24 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[rb][i] = 0.f;
     }
-    auto item = [&](auto ITc) __attribute__((always_inline)) {
-      constexpr int it = decltype(ITc)::value;
-      if constexpr (it < T::IT_STATS) {  // row-max partial over 8 scores
-        constexpr int rb = it / T::NMAXP, k = it % T::NMAXP, kb2 = k >> 1, r0 = (k & 1) * 8;
+    // Vector-ALU work placed after matrix-product slot SL (4 slots per step).
+    // Slots [0, SL_STATS): one row-max chain over 8 scores each; then the
+    // running statistics of each row block; then groups of 4 probabilities,
+    // each moving through three stages on consecutive slots (FMA, exp2, pack
+    // and sum), so no instruction waits right behind its producer; then the
+    // running sums.
+    auto slot_work = [&](auto SLc) __attribute__((always_inline)) {
+      constexpr int sl = decltype(SLc)::value;
+      if constexpr (sl < T::SL_STATS) {
+        constexpr int rb = sl % 2, k = sl / 2, kb2 = k >> 1, r0 = (k & 1) * 8;
         const f32x16& x = s_cur[rb][kb2];
-        mxp[rb][k] = fmaxf(fmaxf(fmaxf(x[r0], x[r0 + 1]), fmaxf(x[r0 + 2], x[r0 + 3])),
-                           fmaxf(fmaxf(x[r0 + 4], x[r0 + 5]), fmaxf(x[r0 + 6], x[r0 + 7])));
-      } else if constexpr (it < T::IT_PAIRS) {  // running statistics
-        constexpr int rb = it - T::IT_STATS;
+        float mm = fmaxf(fmaxf(x[r0], x[r0 + 1]), x[r0 + 2]);
+        mm = fmaxf(fmaxf(mm, x[r0 + 3]), x[r0 + 4]);
+        mm = fmaxf(fmaxf(mm, x[r0 + 5]), x[r0 + 6]);
+        mxp[rb][k] = fmaxf(mm, x[r0 + 7]);
+        pin(mxp[rb][k]);
+      } else if constexpr (sl < T::SL_GROUPS) {
+        constexpr int rb = sl - T::SL_STATS;
         float mx = mxp[rb][0];
         static_for<1, T::NMAXP>([&](auto Kc) __attribute__((always_inline)) {
           mx = fmaxf(mx, mxp[rb][decltype(Kc)::value]);
@@ -415,28 +431,52 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
         mx = halves_max(mx);
         const float mt = mx * c;  // -inf stays -inf (c > 0)
         const float m_new = (mt > m[rb] + 8.f) ? mt : m[rb];
-        alpha[rb] = (m_new == m[rb]) ? 1.f : fast_exp2(m[rb] - m_new);
+        // Tile 0 holds key 0 for every row, so m_new is finite from the
+        // first tile on; exp2(0) = 1 exactly when the reference stays.
+        alpha[rb] = fast_exp2(m[rb] - m_new);
         m[rb] = m_new;
         base[rb] = m_new;
-      } else if constexpr (it < T::IT_SUMS) {  // one pair of probabilities
-        constexpr int pi = it - T::IT_PAIRS, rb = pi & 1, p = pi >> 1, kb2 = p >> 3, jj = p & 7;
-        const float p0 = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][2 * jj], c, -base[rb]));
-        const float p1 = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][2 * jj + 1], c, -base[rb]));
-        pk_cur[rb][kb2][jj] = pack_bf16x2(p0, p1);
-        rs[rb][p & 3] += p0 + p1;
-      } else {  // running sum
-        constexpr int rb = it - T::IT_SUMS;
+        pin(alpha[rb]);
+        pin(base[rb]);
+      } else if constexpr (sl < T::SL_SUMS) {
+        constexpr int t = sl - T::SL_GROUPS, g = t / 3, stage = t % 3;
+        constexpr int rb = g & 1, eg = g >> 1, kb2 = eg >> 2, r0 = (eg & 3) * 4;
+        if constexpr (stage == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xg[g][e] = __builtin_fmaf(s_cur[rb][kb2][r0 + e], c, -base[rb]);
+            pin(xg[g][e]);
+          }
+        } else if constexpr (stage == 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xg[g][e] = fast_exp2(xg[g][e]);
+            pin(xg[g][e]);
+          }
+        } else {
+          pk_cur[rb][kb2][r0 / 2] = pack_bf16x2(xg[g][0], xg[g][1]);
+          pk_cur[rb][kb2][r0 / 2 + 1] = pack_bf16x2(xg[g][2], xg[g][3]);
+          rs[rb][eg & 3] += (xg[g][0] + xg[g][1]) + (xg[g][2] + xg[g][3]);
+          pin(pk_cur[rb][kb2][r0 / 2]);
+          pin(pk_cur[rb][kb2][r0 / 2 + 1]);
+          pin(rs[rb][eg & 3]);
+        }
+      } else if constexpr (sl < T::SL_SUMS + T::RB) {
+        constexpr int rb = sl - T::SL_SUMS;
         l[rb] = alpha[rb] * l[rb] + ((rs[rb][0] + rs[rb][1]) + (rs[rb][2] + rs[rb][3]));
+        pin(l[rb]);
       }
     };
-    // Runs the softmax item with number IT if it belongs to the range [B, E).
-    auto item_if = [&](auto ITc, auto Bc, auto Ec) __attribute__((always_inline)) {
-      constexpr int it = decltype(ITc)::value;
-      if constexpr (it >= decltype(Bc)::value && it < decltype(Ec)::value) item(IC<it>{});
+
+    // All program slots mapped to physical slot P.
+    auto run_slot = [&](auto Pc) __attribute__((always_inline)) {
+      constexpr int p = decltype(Pc)::value;
+      static_for<T::prog_begin(p), T::prog_begin(p + 1)>(
+          [&](auto SLc) __attribute__((always_inline)) { slot_work(SLc); });
     };
 
-    // 16 steps: score product of K fragment i for both row blocks, value
-    // product of V fragment i for both row blocks, softmax items in between.
+    // NFRAG steps: score products of K fragment i (both row blocks), value
+    // products of V fragment i (both row blocks), slot work after each.
     u32x4 ka[T::NFRAG], va[T::NFRAG];
     ka[0] = kread(kb, 0);
     ka[1] = kread(kb, 1);
@@ -447,7 +487,6 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, T::NFRAG>([&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
-      constexpr int ib = T::item_begin(i), ie = T::item_end(i);
       if constexpr (i + 2 < T::NFRAG) {
         ka[i + 2] = kread(kb, i + 2);
         if constexpr (!FIRST) va[i + 2] = vread(vb, i + 2);
@@ -463,30 +502,23 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
         } else {
           s_next[rb][kb2] = mma(as_bf16x8(ka[i]), qf[rb][ks], s_next[rb][kb2]);
         }
-        item_if(IC<ib + rb>{}, IC<ib>{}, IC<ie>{});
+        run_slot(IC<4 * i + rb>{});
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (!FIRST) {
-        constexpr int step = i / T::DB, db = i % T::DB, kb2 = step >> 1, hf = step & 1;
-        static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
-          constexpr int rb = decltype(RBc)::value;
+      static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
+        constexpr int rb = decltype(RBc)::value;
+        if constexpr (!FIRST) {
+          constexpr int step = i / T::DB, db = i % T::DB, kb2 = step >> 1, hf = step & 1;
           u32x4 bp;
           bp.x = pk_prev[rb][kb2][hf * 4 + 0];
           bp.y = pk_prev[rb][kb2][hf * 4 + 1];
           bp.z = pk_prev[rb][kb2][hf * 4 + 2];
           bp.w = pk_prev[rb][kb2][hf * 4 + 3];
           oacc[rb][db] = mma(as_bf16x8(va[i]), as_bf16x8(bp), oacc[rb][db]);
-          item_if(IC<ib + 2 + rb>{}, IC<ib>{}, IC<ie>{});
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else {
-        item_if(IC<ib + 2>{}, IC<ib>{}, IC<ie>{});
-        item_if(IC<ib + 3>{}, IC<ib>{}, IC<ie>{});
-      }
-      // Items beyond four in this step.
-      static_for<ib + 4, (ie > ib + 4 ? ie : ib + 4)>(
-          [&](auto ITc) __attribute__((always_inline)) { item(ITc); });
-      __builtin_amdgcn_sched_barrier(0);
+        }
+        run_slot(IC<4 * i + 2 + rb>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
     // Rescale after P(j-1)V(j-1) is in, before P(j)V(j) is added.
     if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
