@@ -31,6 +31,7 @@ struct BwdArgs {
   void* dK;
   void* dV;
   float* Dvec;   // [BH, Lq] row statistic (workspace)
+  float* lse2;   // [BH, Lq] lse * log2(e) (workspace, bf16 path only)
   float* dQacc;  // [BH, Lq, d] fp32 accumulator (workspace, bf16 path only)
   int BH, Lq, Lk, d;
   float scale;

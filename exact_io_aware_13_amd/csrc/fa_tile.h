@@ -1,0 +1,96 @@
+// LDS tile helpers shared by the bf16 matrix-core kernels: chunk swizzle,
+// plain and transposing LDS fragment reads, wait-count and barrier
+// primitives, compile-time loops, and the wave-half exchange.  Internal to
+// libfa.
+#pragma once
+
+#include "fa_device.h"
+
+#include <type_traits>
+
+namespace fa {
+
+// Chunk swizzle: bijective on the row index mod 16 (d=128) or on row/2 mod 8
+// (d=64), and spreads the 4 rows of a transposed read over all banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// s_waitcnt vmcnt(N) leaving expcnt and lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier that leaves buffer loads in flight: completes this wave's
+// LDS reads (lgkmcnt(0)), then s_barrier.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// Pins a value at this point of the instruction stream: the empty asm
+// "modifies" it, so it must be computed before and cannot be sunk past it.
+// Keeps the hand-placed softmax work between the matrix products it is meant
+// to overlap (scheduling barriers alone do not stop code sinking).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+
+// Calls f(IC<B>{}), ..., f(IC<E-1>{}): loop bodies with compile-time indices,
+// so register arrays are never indexed at run time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Row max / row sum across the two wave halves (lanes l and l ^ 32 hold the
+// two halves of one query row).  v_permlane32_swap exchanges the upper 32
+// lanes of its first operand with the lower 32 lanes of its second; applied
+// to two copies of x, every lane ends up with its own value in one register
+// and its partner's in the other.  Issued as a single VALU instruction in
+// asm: given identical operands, the compiler otherwise treats the two
+// results of the builtin as equal and drops one.
+__device__ __forceinline__ void halves_pair(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  // The nops give the wait states a VALU write needs before the swap reads
+  // it (the compiler cannot see hazards inside asm).
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return a + b;
+}
+
+}  // namespace fa
