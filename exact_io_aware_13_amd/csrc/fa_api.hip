@@ -95,10 +95,8 @@ size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H, int64_t L
   if (!valid_dtype(in_dtype) || check_shape(in_dtype, B, H, Lq, Lk, d) != FA_OK) return 0;
   const size_t rows = (size_t)(B * H * Lq);
   const size_t stat = round_up(rows * sizeof(float), 256);
-  size_t bytes = stat;  // D statistic
-  // bf16: lse in base 2 and the fp32 dQ accumulator.
-  if (in_dtype == FA_BF16) bytes += stat + rows * (size_t)d * sizeof(float);
-  return bytes;
+  // D statistic; bf16 also keeps lse in base 2.
+  return in_dtype == FA_BF16 ? 2 * stat : stat;
 }
 
 fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
@@ -130,10 +128,10 @@ fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk
   a.dK = dK;
   a.dV = dV;
   const size_t stat = round_up(rows * sizeof(float), 256);
-  const bool split = in_dtype == FA_BF16 && workspace;
   a.Dvec = static_cast<float*>(workspace);
-  a.lse2 = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stat) : nullptr;
-  a.dQacc = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * stat) : nullptr;
+  a.lse2 = in_dtype == FA_BF16 && workspace
+               ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stat)
+               : nullptr;
   a.BH = (int)(B * H);
   a.Lq = (int)Lq;
   a.Lk = (int)Lk;

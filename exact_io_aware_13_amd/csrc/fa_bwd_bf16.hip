@@ -455,6 +455,7 @@ struct DqTile {
   // Products per iteration: S^T of tile j, dP^T of tile j, dQ^T of tile j-1.
   static constexpr int NS = RB * NFRAG, NP = RB * NFRAG, NQ = RB * NT;
   static constexpr int NDS = RB * NKB * 4;        // 4-element groups per tile
+  static constexpr int GLOADS = BR * ROWB / 1024 / NW;  // dO rows: load instructions per wave
   static_assert(LOADS >= 1, "tile split");
 };
 
@@ -474,6 +475,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char V1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V2[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V3[T::TILEB];
+  // The workgroup's dO rows stay in LDS for the whole kernel: B operands of
+  // dP^T.  (Q's rows stay in registers; both would not fit next to the dQ
+  // accumulators.)
+  __shared__ __attribute__((aligned(1024))) char GR[T::BR * T::ROWB];
   auto kslot = [&](auto I) __attribute__((always_inline)) -> char* {
     constexpr int v = decltype(I)::value;
     if constexpr (v == 0) return K0;
@@ -570,21 +575,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     return a;
   };
 
-  // ---- per-row operands: Q and dO rows (B operands), lse2 and D -------------
-  bf16x8 qf[T::RB][T::KS], gf[T::RB][T::KS];
+  // ---- per-row operands: Q rows (B operands of S^T), lse2 and D -------------
+  bf16x8 qf[T::RB][T::KS];
   float lse2[T::RB], dd[T::RB];
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb) {
     const int qrow = qw0 + 32 * rb + n;
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      const uint32_t off = (uint32_t)(qrow * D + ks * 16 + h * 8) * 2;
-      qf[rb][ks] = as_bf16x8(load16(rq, off));
-      gf[rb][ks] = as_bf16x8(load16(rdo, off));
-    }
+    for (int ks = 0; ks < T::KS; ++ks)
+      qf[rb][ks] = as_bf16x8(load16(rq, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2));
     lse2[rb] = load4f(rl, (uint32_t)qrow * 4);
     dd[rb] = load4f(re, (uint32_t)qrow * 4);
   }
+  // dO rows [q0, q0 + BR) into GR (same swizzled layout as the K/V tiles).
+#pragma unroll
+  for (int i = 0; i < T::GLOADS; ++i) {
+    const int row = (w * T::GLOADS + i) * T::RPK + lane / T::CPR;
+    const int chunk = (lane % T::CPR) ^ swz<D>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (lds_void*)(GR + (w * T::GLOADS + i) * 1024), 16,
+                                             (uint32_t)((q0 + row) * D + chunk * 8) * 2, 0, 0, 0);
+  }
+  // dO fragment of row block rb, step ks (B operand of dP^T).
+  auto gread = [&](int rb, int ks) __attribute__((always_inline)) {
+    return lds_read16(GR, (64 * w + 32 * rb) * T::ROWB + koffs[ks]);
+  };
 
   f32x16 dq[T::RB][T::DB];
 #pragma unroll
@@ -640,10 +654,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
     f32x16 s[T::RB][T::NKB], dpv[T::RB][T::NKB];
     float pv[T::RB][T::NKB][16];
-    u32x4 afr[NALL];
-    // One LDS fragment feeds both row blocks.
+    u32x4 afr[NALL], bfr[T::NP];
+    // One K / V / K^T fragment feeds both row blocks; dP^T also reads its
+    // dO fragment.
     auto read_frag = [&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
+      if constexpr (i >= T::NS && i < N1) {
+        constexpr int x = i - T::NS, f = x / T::RB;
+        bfr[x] = gread(x % T::RB, f / T::NKB);
+      }
       if constexpr (i % T::RB == 0) {
         if constexpr (i < T::NS) afr[i] = fread(kb_, i / T::RB);
         else if constexpr (i < N1) afr[i] = fread(vb_, (i - T::NS) / T::RB);
@@ -660,7 +679,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         s[rb][kb] = mma(as_bf16x8(afr[i0]), qf[rb][ks], ks == 0 ? z : s[rb][kb]);
       } else if constexpr (i < N1) {
         constexpr int f = (i - T::NS) / T::RB, kb = f % T::NKB, ks = f / T::NKB;
-        dpv[rb][kb] = mma(as_bf16x8(afr[i0]), gf[rb][ks], ks == 0 ? z : dpv[rb][kb]);
+        dpv[rb][kb] = mma(as_bf16x8(afr[i0]), as_bf16x8(bfr[i - T::NS]), ks == 0 ? z : dpv[rb][kb]);
       } else {
         dq_product(afr[i0], ds_prev, IC<(i - N1) / T::RB>{}, IC<rb>{});
       }
@@ -732,7 +751,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     block_barrier();
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 landed ------------------------
+  // ---- prologue: dO rows and tile 0 landed, tile 1 in flight -------------------
   fetch(0, IC<0>{});
   __builtin_amdgcn_sched_barrier(0);  // tile 0's loads are issued first
   fetch(1, IC<1>{});

@@ -32,7 +32,6 @@ struct BwdArgs {
   void* dV;
   float* Dvec;   // [BH, Lq] row statistic (workspace)
   float* lse2;   // [BH, Lq] lse * log2(e) (workspace, bf16 path only)
-  float* dQacc;  // [BH, Lq, d] fp32 accumulator (workspace, bf16 path only)
   int BH, Lq, Lk, d;
   float scale;
   bool causal;

@@ -103,10 +103,9 @@ FA_API fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: the D statistic
- * ([B,H,Lq] float) and, for bf16, lse in base 2 ([B,H,Lq] float) and an
- * fp32 dQ accumulator ([B,H,Lq,d]); each [B,H,Lq] part is padded to a
- * multiple of 256 bytes.  Linear in Lq; independent of the number of
- * scores.  Returns 0 for sizes fa_bwd would reject.
+ * ([B,H,Lq] float) and, for bf16, lse in base 2 ([B,H,Lq] float); each
+ * part is padded to a multiple of 256 bytes.  Linear in Lq; independent of
+ * the number of scores.  Returns 0 for sizes fa_bwd would reject.
  */
 FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
                               int64_t Lq, int64_t Lk, int64_t d);

@@ -107,8 +107,8 @@ def test_workspace_is_linear_in_length(lib):
     L, L2 = mem["L"], mem["L_doubled"]
     w1 = lib.fa_bwd_workspace_bytes(BF16, 1, 1, L, L, 128)
     w2 = lib.fa_bwd_workspace_bytes(BF16, 1, 1, L2, L2, 128)
-    # D statistic, base-2 lse and fp32 dQ accumulator: exactly L*(8 + 4d) bytes here.
-    assert w1 == 2 * L * 4 + L * 128 * 4
+    # D statistic and base-2 lse: exactly 2 * 4 L bytes here.
+    assert w1 == 2 * L * 4
     assert w2 == 2 * w1                               # linear in L ...
     assert mem["MiB_doubled"] == mem["growth_when_L_doubles"] * mem["MiB"]  # ... the scores grow 4x
     assert mem["elements"] == L * L and mem["bytes"] == L * L * mem["bytes_per_element"]
@@ -116,7 +116,7 @@ def test_workspace_is_linear_in_length(lib):
     assert lib.fa_bwd_workspace_bytes(F32, 1, 1, L, L, 128) == L * 4
     assert lib.fa_bwd_workspace_bytes(BF16, 1, 1, L, L, 96) == 0
     for L_ in (1024, 2048, 4096, 8192):
-        assert lib.fa_bwd_workspace_bytes(BF16, 1, 32, L_, L_, 128) == 32 * L_ * (8 + 512)
+        assert lib.fa_bwd_workspace_bytes(BF16, 1, 32, L_, L_, 128) == 32 * L_ * 8
 
 
 def test_one_hip_runtime_is_mapped(lib):

@@ -72,16 +72,16 @@ def test_forward_is_bitwise_deterministic():
     assert torch.equal(runs[2][0], runs[3][0]) and torch.equal(runs[2][1], runs[3][1])
 
 
-def test_backward_key_gradients_deterministic_query_gradient_bounded():
-    # dK and dV are owned by one workgroup each: bitwise reproducible.  dQ is
-    # summed with fp32 atomics across key tiles, so its bits may differ in
-    # the last place between runs.
-    q, k, v, do = to_dev(*make_inputs(1, 8, 2048, 2048, 128, "bf16", seed=6, with_dO=True))
+def test_backward_is_bitwise_deterministic():
+    # Every gradient row is owned by one workgroup and summed in a fixed
+    # order (no atomics), so repeated calls agree bit for bit, with and
+    # without the causal mask and with a ragged length.
+    q, k, v, do = to_dev(*make_inputs(1, 8, 2000, 2000, 128, "bf16", seed=6, with_dO=True))
     announce("determinism: backward")
-    O, lse = fa.fa_fwd(q, k, v, causal=True)
-    g1 = fa.fa_bwd(q, k, v, O, do, lse, causal=True)
-    g2 = fa.fa_bwd(q, k, v, O, do, lse, causal=True)
-    torch.cuda.synchronize()
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    diff = (g1[0].float() - g2[0].float()).abs().max().item()
-    assert diff <= 1e-2 * g1[0].float().abs().max().item()
+    for causal in (True, False):
+        O, lse = fa.fa_fwd(q, k, v, causal=causal)
+        g1 = fa.fa_bwd(q, k, v, O, do, lse, causal=causal)
+        g2 = fa.fa_bwd(q, k, v, O, do, lse, causal=causal)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
