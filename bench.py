@@ -1,22 +1,29 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
-One step is one pass of the whole hot path over one batch: fa_fwd (O, lse)
-then fa_bwd (D statistic, dQ/dK/dV) through the C ABI, at B1 H32 L4096
-d128, causal, bf16 inputs with fp32 accumulation.  Inputs, outputs and the
-workspace are resident in device memory before timing starts.
+One step is one pass of the whole hot path over one batch through the C ABI:
+fa_fwd (O, lse), then the backward's three stages fa_bwd_prepare (D, base-2
+lse), fa_bwd_dkdv and fa_bwd_dq -- together exactly fa_bwd -- at B1 H32
+L4096 d128, causal, bf16 inputs with fp32 accumulation.  Inputs, outputs and
+the workspace are resident in device memory before timing starts.
 
-Throughput uses the algorithmic FLOP count: forward 4*B*H*Lq*Lk*d, halved
-for the causal mask, backward 2.5x the forward.  The line also carries the
-dominant kernel's roofline position (timed with HIP events on the stream the
-library launches on) and the fp64 CPU oracle timed on a bounded sample of
-the same workload.
+Throughput uses the algorithmic FLOP count: forward 4*B*H*Lq*Lk*d, halved for
+the causal mask, backward 2.5x the forward (five matrix products).  The dQ
+kernel recomputes S and dP, which the count does not credit.
+
+Every kernel is timed with HIP events recorded on the stream the library
+launches on (torch's current stream, passed to every call).  The line carries
+the roofline position of the kernel with the largest measured time: its
+algorithmic FLOPs per launch over its average duration, against the bf16
+matrix-core peak, and -- when a counter summary for the current kernel source
+exists under profiles/ -- the HBM bytes measured by rocprofv3.  The fp64 CPU
+oracle is timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -32,6 +39,8 @@ from workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs  # noqa: E402
 METRIC = "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B1 H32 L4096 d128 causal"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak (published)
+CSRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def flops(B, H, Lq, Lk, d, causal):
@@ -39,18 +48,48 @@ def flops(B, H, Lq, Lk, d, causal):
     return fwd, 2.5 * fwd
 
 
-def hbm_bytes(B, H, Lq, Lk, d):
-    """Algorithmic bytes: each tensor read or written once (bf16, fp32 stats)."""
-    q, kv = B * H * Lq * d * 2, B * H * Lk * d * 2
-    stats = B * H * Lq * 4
-    fwd = q + 2 * kv + q + stats                            # Q, K, V in; O, lse out
-    bwd = (q + 2 * kv + q + q + stats) + (q + 2 * kv)       # Q K V O dO lse in; dQ dK dV out
-    return fwd, bwd
+def kernel_table(B, H, L, d):
+    """Per kernel: source file, algorithmic FLOPs and HBM bytes per launch.
+
+    One matrix product over the visible (query, key) pairs is f1 = fwd / 2.
+    The forward does 2 (S, PV); dK/dV does 4 of the backward's 5 (S, dP, dV,
+    dK); dQ does 1 algorithmic product (dQ) plus S and dP again.  Bytes:
+    every tensor the kernel must touch, read or written once.
+    """
+    f_fwd, _ = flops(B, H, L, L, d, True)
+    f1 = f_fwd / 2
+    t = B * H * L * d * 2          # one [B,H,L,d] bf16 tensor
+    r = B * H * L * 4              # one [B,H,L] fp32 row vector
+    return {
+        "fwd_bf16_kernel": dict(src="fa_fwd_bf16.hip", flops=2 * f1, executed=2 * f1,
+                                bytes=3 * t + t + r),
+        "bwd_pre_bf16_kernel": dict(src="fa_bwd_bf16.hip", flops=0.0, executed=0.0,
+                                    bytes=2 * t + r + 2 * r),
+        "bwd_dkdv_kernel": dict(src="fa_bwd_bf16.hip", flops=4 * f1, executed=4 * f1,
+                                bytes=4 * t + 2 * r + 2 * t),
+        "bwd_dq_kernel": dict(src="fa_bwd_bf16.hip", flops=1 * f1, executed=3 * f1,
+                              bytes=4 * t + 2 * r + t),
+    }
+
+
+def source_hash(name):
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel, src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{kernel}_B1H32L4096d128_causal_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_hash(src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(w, seconds_target=15.0):
     """The fp64 oracle (forward + backward) on whole heads of the workload."""
-    import numpy as np
     import oracle
     from workloads import to_f64
     try:
@@ -109,21 +148,28 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.fa_bwd_workspace_bytes(torch.bfloat16, B, H, L, L, d), dtype=torch.uint8,
                      device=dev)
+    names = ["fwd_bf16_kernel", "bwd_pre_bf16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
 
     def step(ev=None):
+        # Events go on torch's current stream, the stream every call below
+        # launches its kernel on.
+        calls = [
+            lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=lse),
+            lambda: fa.fa_bwd_prepare(O, do, lse, L, ws),
+            lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, scale=w.scale, causal=True, dk=dk, dv=dv),
+            lambda: fa.fa_bwd_dq(q, k, v, do, ws, scale=w.scale, causal=True, dq=dq),
+        ]
+        for i, call in enumerate(calls):
+            if ev is not None:
+                ev[i].record()
+            call()
         if ev is not None:
-            ev[0].record()
-        fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=lse)
-        if ev is not None:
-            ev[1].record()
-        fa.fa_bwd(q, k, v, O, do, lse, scale=w.scale, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
-        if ev is not None:
-            ev[2].record()
+            ev[len(calls)].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -132,19 +178,26 @@ def main():
         step(evs[i])
     t_end.record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
 
     f_fwd, f_bwd = flops(B, H, L, L, d, True)
-    b_fwd, b_bwd = hbm_bytes(B, H, L, L, d)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    if bwd_ms >= fwd_ms:
-        dom, dom_flops, dom_ms, dom_bytes = "fa_bwd (bwd_pre, bwd_main, dq_convert)", f_bwd, bwd_ms, b_bwd
-    else:
-        dom, dom_flops, dom_ms, dom_bytes = "fwd_bf16_kernel", f_fwd, fwd_ms, b_fwd
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    table = kernel_table(B, H, L, d)
+    kernels = {}
+    for n in names:
+        t = table[n]
+        s = kms[n] * 1e-3
+        kernels[n] = {"ms": round(kms[n], 4),
+                      "algorithmic_tflops": round(t["flops"] / s / 1e12, 2),
+                      "executed_tflops": round(t["executed"] / s / 1e12, 2),
+                      "algorithmic_gbs": round(t["bytes"] / s / 1e9, 1)}
+    dom = max(names, key=lambda n: kms[n])
+    t = table[dom]
+    achieved = t["flops"] / (kms[dom] * 1e-3) / 1e12
+    traffic = measured_traffic(dom, t["src"])
+    fwd_ms = kms["fwd_bf16_kernel"]
+    bwd_ms = sum(kms[n] for n in names[1:])
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -166,11 +219,11 @@ def main():
                 "pct_peak": round(100 * f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
                 "pct_peak": round(100 * f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "algorithmic_bytes": dom_bytes,
-                     "algorithmic_gbs": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": t["bytes"]},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

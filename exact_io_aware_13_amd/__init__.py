@@ -6,12 +6,15 @@ exposes the same calls on torch tensors:
 
     fa_fwd(q, k, v, scale, causal)            -> (O, lse)
     fa_bwd(q, k, v, o, do, lse, scale, causal) -> (dQ, dK, dV)
+    fa_bwd_prepare / fa_bwd_dkdv / fa_bwd_dq     (the backward's stages)
     fa_bwd_workspace_bytes(dtype, B, H, Lq, Lk, d)
     attention(q, k, v, causal=False, scale=None)   (autograd)
 """
 
-from .binding import FlashAttentionFn, attention, fa_bwd, fa_bwd_workspace_bytes, fa_fwd
+from .binding import (FlashAttentionFn, attention, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
+                      fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd)
 from ._lib import FaError, LIB_PATH, load as load_library
 
-__all__ = ["attention", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "FlashAttentionFn",
+__all__ = ["attention", "fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_workspace_bytes", "FlashAttentionFn",
            "FaError", "LIB_PATH", "load_library"]

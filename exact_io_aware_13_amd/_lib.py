@@ -21,7 +21,8 @@ STATUS_NAMES = {
     4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG",
 }
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_workspace_bytes", "fa_status_str", "fa_version")
 
 _lib = None
 
@@ -42,6 +43,14 @@ def _declare(lib):
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
                            vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_prepare.restype = i32
+    lib.fa_bwd_prepare.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_dkdv.restype = i32
+    lib.fa_bwd_dkdv.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, vp, vp,
+                                ctypes.c_size_t, vp]
+    lib.fa_bwd_dq.restype = i32
+    lib.fa_bwd_dq.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, vp,
+                              ctypes.c_size_t, vp]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.fa_status_str.restype = ctypes.c_char_p

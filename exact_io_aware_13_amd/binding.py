@@ -1,7 +1,8 @@
 """Python binding of libfa with the C ABI's names.
 
-``fa_fwd`` / ``fa_bwd`` / ``fa_bwd_workspace_bytes`` only marshal torch
-tensors (device pointers, sizes, the current HIP stream) into the C calls;
+``fa_fwd``, ``fa_bwd`` (and its stages ``fa_bwd_prepare``, ``fa_bwd_dkdv``,
+``fa_bwd_dq``) and ``fa_bwd_workspace_bytes`` only marshal torch tensors
+(device pointers, sizes, the current HIP stream) into the C calls;
 all arithmetic runs in the library's HIP kernels.  PyTorch supplies device
 memory and streams.  ``attention`` wraps both calls in an autograd Function
 with the signature of the annotated-code page's usage example,
@@ -116,6 +117,65 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
                     _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(st)
     return dq, dk, dv
+
+
+def _bwd_shapes(q, k, v, do):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
+                         ("do", do, (B, H, Lq, d))):
+        _check_tensor(name, t, dev, q.dtype, shp)
+    return B, H, Lq, Lk, d, dev
+
+
+def fa_bwd_prepare(o, do, lse, Lk, workspace):
+    """Stage 1 of ``fa_bwd``: per-row statistics into ``workspace``.
+
+    ``Lk`` is the key length of the later stages (it sizes the checks).
+    """
+    B, H, Lq, d = o.shape
+    dev = o.device
+    _check_tensor("o", o, dev)
+    _check_tensor("do", do, dev, o.dtype, o.shape)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_bwd_prepare(_code(o.dtype), B, H, Lq, Lk, d, _ptr(o), _ptr(do), _ptr(lse),
+                                    _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+
+
+def fa_bwd_dkdv(q, k, v, do, workspace, scale=None, causal=False, dk=None, dv=None):
+    """Stage 2 of ``fa_bwd``: dK and dV from a prepared workspace."""
+    B, H, Lq, Lk, d, dev = _bwd_shapes(q, k, v, do)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dk", dk, dev, q.dtype, k.shape)
+    _check_tensor("dv", dv, dev, q.dtype, v.shape)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_bwd_dkdv(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(do), float(scale), int(bool(causal)), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return dk, dv
+
+
+def fa_bwd_dq(q, k, v, do, workspace, scale=None, causal=False, dq=None):
+    """Stage 3 of ``fa_bwd``: dQ from a prepared workspace."""
+    B, H, Lq, Lk, d, dev = _bwd_shapes(q, k, v, do)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_tensor("dq", dq, dev, q.dtype, q.shape)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_bwd_dq(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                               float(scale), int(bool(causal)), _ptr(dq), _ptr(workspace),
+                               workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return dq
 
 
 class FlashAttentionFn(torch.autograd.Function):

@@ -94,21 +94,31 @@ size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H, int64_t L
                               int64_t d) {
   if (!valid_dtype(in_dtype) || check_shape(in_dtype, B, H, Lq, Lk, d) != FA_OK) return 0;
   const size_t rows = (size_t)(B * H * Lq);
-  const size_t stat = round_up(rows * sizeof(float), 256);
-  // D statistic; bf16 also keeps lse in base 2.
-  return in_dtype == FA_BF16 ? 2 * stat : stat;
+  // D statistic and lse in base 2.
+  return 2 * round_up(rows * sizeof(float), 256);
 }
 
-fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
-                 const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                 const float* lse, float scale, int causal, void* dQ, void* dK, void* dV,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by fa_bwd and its three stages: validates exactly the pointers the
+// requested stages touch, then enqueues those stages.
+fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq,
+                     int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
+                     const void* O, const void* dO, const float* lse, float scale, int causal,
+                     void* dQ, void* dK, void* dV, const void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
   if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
   if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
   const bool has_q = B * H * Lq > 0, has_k = B * H * Lk > 0;
   if (!has_q && !has_k) return FA_OK;
-  if (has_q && (!Q || !O || !dO || !lse || !dQ)) return FA_ERR_NULL;
-  if (has_k && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
+  const bool pre = stages & fa::kBwdPrepare, kv = stages & fa::kBwdDkDv, dq = stages & fa::kBwdDq;
+  // A slice with queries always has keys (check_shape), so has_q implies has_k.
+  if (has_q && pre && (!O || !dO || !lse)) return FA_ERR_NULL;
+  if (has_q && (kv || dq) && (!Q || !dO)) return FA_ERR_NULL;
+  if (has_q && dq && (!K || !V || !dQ)) return FA_ERR_NULL;
+  if (has_k && kv && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
   const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FA_ERR_ALIGN;
@@ -117,6 +127,8 @@ fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
 
   const size_t rows = (size_t)(B * H * Lq);
+  const size_t stat = round_up(rows * sizeof(float), 256);
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
   fa::BwdArgs a;
   a.Q = Q;
   a.K = K;
@@ -127,19 +139,58 @@ fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk
   a.dQ = dQ;
   a.dK = dK;
   a.dV = dV;
-  const size_t stat = round_up(rows * sizeof(float), 256);
-  a.Dvec = static_cast<float*>(workspace);
-  a.lse2 = in_dtype == FA_BF16 && workspace
-               ? reinterpret_cast<float*>(static_cast<char*>(workspace) + stat)
-               : nullptr;
+  a.Dvec = reinterpret_cast<float*>(ws);
+  a.lse2 = ws ? reinterpret_cast<float*>(ws + stat) : nullptr;
   a.BH = (int)(B * H);
   a.Lq = (int)Lq;
   a.Lk = (int)Lk;
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal != 0;
-  const hipError_t e = in_dtype == FA_BF16 ? fa::launch_bwd_bf16(a, stream) : fa::launch_bwd_f32(a, stream);
+  // Second line of defence: every pointer a launched kernel dereferences is
+  // set (the checks above are per argument; this is per kernel).
+  if (has_q && pre && !(a.O && a.dO && a.lse && a.Dvec && a.lse2)) return FA_ERR_NULL;
+  if (has_k && kv && !(a.K && a.V && a.dK && a.dV)) return FA_ERR_NULL;
+  if (has_q && kv && !(a.Q && a.dO && a.Dvec && a.lse2)) return FA_ERR_NULL;
+  if (has_q && dq && !(a.Q && a.K && a.V && a.dO && a.dQ && a.Dvec && a.lse2)) return FA_ERR_NULL;
+  const hipError_t e = in_dtype == FA_BF16 ? fa::launch_bwd_bf16(a, stages, stream)
+                                           : fa::launch_bwd_f32(a, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* lse, float scale, int causal, void* dQ, void* dK, void* dV,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_stages(fa::kBwdAll, in_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale, causal,
+                    dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_prepare(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                         int64_t d, const void* O, const void* dO, const float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_stages(fa::kBwdPrepare, in_dtype, B, H, Lq, Lk, d, nullptr, nullptr, nullptr, O, dO,
+                    lse, 1.f, 0, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_dkdv(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                      const void* Q, const void* K, const void* V, const void* dO, float scale,
+                      int causal, void* dK, void* dV, const void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return bwd_stages(fa::kBwdDkDv, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO, nullptr, scale,
+                    causal, nullptr, dK, dV, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_dq(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                    const void* Q, const void* K, const void* V, const void* dO, float scale,
+                    int causal, void* dQ, const void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return bwd_stages(fa::kBwdDq, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO, nullptr, scale,
+                    causal, dQ, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -804,7 +804,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 template <int D, bool CAUSAL>
-void launch_main(const BwdArgs& a, hipStream_t stream) {
+void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   using TK = KvTile<D>;
   using TQ = DqTile<D>;
   const float c = a.scale * kLog2e;
@@ -813,37 +813,37 @@ void launch_main(const BwdArgs& a, hipStream_t stream) {
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   const int n_kt = (a.Lk + TK::BK - 1) / TK::BK;
-  if (n_kt > 0)
+  if ((stages & kBwdDkDv) && n_kt > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)), dim3(64 * TK::NW),
                        0, stream, Q, K, V, dO, a.lse2, a.Dvec, static_cast<uint16_t*>(a.dK),
                        static_cast<uint16_t*>(a.dV), a.BH, a.Lq, a.Lk, c, a.scale);
   const int n_qt = (a.Lq + TQ::BR - 1) / TQ::BR;
-  if (n_qt > 0 && a.Lk > 0)
+  if ((stages & kBwdDq) && n_qt > 0 && a.Lk > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(64 * TQ::NW),
                        0, stream, Q, K, V, dO, a.lse2, a.Dvec, static_cast<uint16_t*>(a.dQ), a.BH,
                        a.Lq, a.Lk, n_qt, c, a.scale);
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Lq;
-  if (rows > 0) {
+  if ((stages & kBwdPrepare) && rows > 0) {
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
                        0, stream, static_cast<const uint16_t*>(a.O),
                        static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
   }
-  if (a.causal) launch_main<D, true>(a, stream);
-  else launch_main<D, false>(a, stream);
+  if (a.causal) launch_main<D, true>(a, stages, stream);
+  else launch_main<D, false>(a, stages, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   static_assert(KvTile<128>::BK == kBwdBf16KeysPerBlock, "tile table out of sync");
-  if (a.d == 64) return launch_d<64>(a, stream);
-  return launch_d<128>(a, stream);
+  if (a.d == 64) return launch_d<64>(a, stages, stream);
+  return launch_d<128>(a, stages, stream);
 }
 
 }  // namespace fa

@@ -96,23 +96,26 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict_
   }
 }
 
-// D_i = sum_c dO_ic O_ic, one thread per row.
+// D_i = sum_c dO_ic O_ic and lse in base 2, one thread per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restrict__ O,
                                                           const float* __restrict__ dO,
-                                                          float* __restrict__ Dvec, int64_t rows) {
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ Dvec,
+                                                          float* __restrict__ lse2, int64_t rows) {
   const int64_t r = (int64_t)wg_id() * 256 + wi_id();
   if (r >= rows) return;
   float acc = 0.f;
   for (int c = 0; c < D; ++c) acc = fmaf(O[r * D + c], dO[r * D + c], acc);
   Dvec[r] = acc;
+  lse2[r] = lse[r] * kLog2e;
 }
 
 // dK and dV: one thread per key row j, looping over the queries that see it.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     float* __restrict__ dK, float* __restrict__ dV, int BH, int Lq, int Lk, float scale_log2,
     float scale) {
   __shared__ float Ql[kTile][D];
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
     }
     if (tid < kTile) {
       const bool in = q0 + tid < Lq;
-      Ll[tid] = in ? LSE[(size_t)bh * Lq + q0 + tid] * kLog2e : 0.f;
+      Ll[tid] = in ? LSE2[(size_t)bh * Lq + q0 + tid] : 0.f;
       Dl[tid] = in ? Dvec[(size_t)bh * Lq + q0 + tid] : 0.f;
     }
     __syncthreads();
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     float* __restrict__ dQ, int BH, int Lq, int Lk, float scale_log2, float scale) {
   __shared__ float Kl[kTile][D];
   __shared__ float Vl[kTile][D];
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
     gr[c] = dO[row * D + c];
     accQ[c][tid] = 0.f;
   }
-  const float lse2 = LSE[row] * kLog2e;
+  const float lse2 = LSE2[row];
   const float Di = Dvec[row];
   const float* Kb = K + (size_t)bh * Lk * D;
   const float* Vb = V + (size_t)bh * Lk * D;
@@ -250,23 +253,24 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t bwd_launch(const BwdArgs& a, hipStream_t stream) {
+hipError_t bwd_launch(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Lq;
   const auto* Q = static_cast<const float*>(a.Q);
   const auto* K = static_cast<const float*>(a.K);
   const auto* V = static_cast<const float*>(a.V);
   const auto* G = static_cast<const float*>(a.dO);
-  if (rows > 0)
+  if ((stages & kBwdPrepare) && rows > 0)
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const float*>(a.O), G, a.Dvec, rows);
+                       stream, static_cast<const float*>(a.O), G, a.lse, a.Dvec, a.lse2, rows);
   const int n_kt = (a.Lk + kRows - 1) / kRows;
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)), dim3(kRows),
-                     0, stream, Q, K, V, G, a.lse, a.Dvec, static_cast<float*>(a.dK),
-                     static_cast<float*>(a.dV), a.BH, a.Lq, a.Lk, a.scale * kLog2e, a.scale);
+  if ((stages & kBwdDkDv) && n_kt > 0)
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)), dim3(kRows),
+                       0, stream, Q, K, V, G, a.lse2, a.Dvec, static_cast<float*>(a.dK),
+                       static_cast<float*>(a.dV), a.BH, a.Lq, a.Lk, a.scale * kLog2e, a.scale);
   const int n_qt = (a.Lq + kRows - 1) / kRows;
-  if (n_qt > 0)
+  if ((stages & kBwdDq) && n_qt > 0)
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(kRows),
-                       0, stream, Q, K, V, G, a.lse, a.Dvec, static_cast<float*>(a.dQ), a.BH,
+                       0, stream, Q, K, V, G, a.lse2, a.Dvec, static_cast<float*>(a.dQ), a.BH,
                        a.Lq, a.Lk, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
@@ -278,9 +282,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   return a.causal ? fwd_launch<128, true>(a, stream) : fwd_launch<128, false>(a, stream);
 }
 
-hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return a.causal ? bwd_launch<64, true>(a, stream) : bwd_launch<64, false>(a, stream);
-  return a.causal ? bwd_launch<128, true>(a, stream) : bwd_launch<128, false>(a, stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+  if (a.d == 64)
+    return a.causal ? bwd_launch<64, true>(a, stages, stream) : bwd_launch<64, false>(a, stages, stream);
+  return a.causal ? bwd_launch<128, true>(a, stages, stream) : bwd_launch<128, false>(a, stages, stream);
 }
 
 }  // namespace fa

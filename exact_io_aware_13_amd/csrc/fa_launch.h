@@ -31,16 +31,22 @@ struct BwdArgs {
   void* dK;
   void* dV;
   float* Dvec;   // [BH, Lq] row statistic (workspace)
-  float* lse2;   // [BH, Lq] lse * log2(e) (workspace, bf16 path only)
+  float* lse2;   // [BH, Lq] lse * log2(e) (workspace)
   int BH, Lq, Lk, d;
   float scale;
   bool causal;
 };
 
+// Backward stages, run in this order by the launchers for the stages set in
+// `stages`: per-row statistics (D, and lse in base 2 for bf16) into the
+// workspace, then dK/dV, then dQ.  The last two only read the statistics
+// and are independent of each other.
+enum : unsigned { kBwdPrepare = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u };
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, unsigned stages, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, unsigned stages, hipStream_t stream);
 
 // Work decomposition shared by validation and the launchers.
 constexpr int kFwdBf16RowsPerBlock = 256;

@@ -103,15 +103,24 @@ FA_API fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: the D statistic
- * ([B,H,Lq] float) and, for bf16, lse in base 2 ([B,H,Lq] float); each
- * part is padded to a multiple of 256 bytes.  Linear in Lq; independent of
- * the number of scores.  Returns 0 for sizes fa_bwd would reject.
+ * and lse in base 2 ([B,H,Lq] float each, each padded to a multiple of 256
+ * bytes).  Linear in Lq; independent of the number of scores.  Returns 0
+ * for sizes fa_bwd would reject.
  */
 FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
                               int64_t Lq, int64_t Lk, int64_t d);
 
 /*
  * Backward: dQ, dK, dV from Q, K, V, the forward's O and lse, and dO.
+ * Probabilities are recomputed tile by tile from lse rather than read from
+ * memory, with the row statistic D_i = sum_c dO_ic O_ic ("How Flash
+ * Attention Improves Transformer Memory Efficiency ...", section "Backward
+ * Pass Efficiency"; glossary page "Flash Attention", section "How it
+ * works"); the gradients are the chain rule through the forward:
+ * dV = P^T dO, dS = P * (dO V^T - D), dK = scale dS^T Q, dQ = scale dS K.
+ * Equivalent to fa_bwd_prepare, then fa_bwd_dkdv and fa_bwd_dq on the same
+ * stream.  No atomics: every gradient row is summed in a fixed order by one
+ * workgroup, so results are bitwise reproducible.
  *   in_dtype   dtype of Q, K, V, O, dO, dQ, dK, dV (O and dO must be in
  *              the input dtype; the fp32-output forward is a diagnostic).
  *   lse        the forward's [B,H,Lq] output.
@@ -129,6 +138,49 @@ FA_API fa_status fa_bwd(fa_dtype in_dtype,
                  float scale, int causal,
                  void* dQ, void* dK, void* dV,
                  void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * The backward in three stages, for callers that run dK/dV and dQ on
+ * different streams or time them apart.  Arguments mean what they mean for
+ * fa_bwd, with the same shapes, layouts, alignment and status codes; each
+ * stage validates only the pointers it uses.
+ *
+ * fa_bwd_prepare writes the per-row statistics (D and lse in base 2) into
+ * `workspace`.  It must complete before fa_bwd_dkdv or
+ * fa_bwd_dq starts reading that workspace (same stream, or an event).
+ */
+FA_API fa_status fa_bwd_prepare(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* O, const void* dO, const float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * fa_bwd_dkdv writes dK and dV ([B,H,Lk,d]); it reads the prepared
+ * workspace and does not modify it.  Key-stationary: each workgroup owns a
+ * block of keys and sums over every query tile that can see them.
+ */
+FA_API fa_status fa_bwd_dkdv(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V, const void* dO,
+                 float scale, int causal,
+                 void* dK, void* dV,
+                 const void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * fa_bwd_dq writes dQ ([B,H,Lq,d]); it reads the prepared workspace and
+ * does not modify it.  Query-stationary: each workgroup owns a block of
+ * queries and sums over every key tile they can see.  It may run
+ * concurrently with fa_bwd_dkdv.
+ */
+FA_API fa_status fa_bwd_dq(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V, const void* dO,
+                 float scale, int causal,
+                 void* dQ,
+                 const void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
 /* Static description of a status code; never NULL. */

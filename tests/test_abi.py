@@ -97,6 +97,54 @@ def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+def _stage(lib, name, in_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125,
+           causal=1, ws=P, ws_bytes=None):
+    p = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dQ=P, dK=P, dV=P)
+    p.update(ptrs or {})
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(in_dt, B, H, Lq, Lk, d)
+    if name == "prepare":
+        return lib.fa_bwd_prepare(in_dt, B, H, Lq, Lk, d, p["O"], p["dO"], p["lse"], ws, ws_bytes,
+                                  None)
+    if name == "dkdv":
+        return lib.fa_bwd_dkdv(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["dO"], scale,
+                               causal, p["dK"], p["dV"], ws, ws_bytes, None)
+    return lib.fa_bwd_dq(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["dO"], scale, causal,
+                         p["dQ"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    ("prepare", dict(in_dt=4), ARG), ("prepare", dict(Lk=0), SHAPE), ("prepare", dict(d=48), UNSUP),
+    ("prepare", dict(ptrs=dict(O=None)), NULL), ("prepare", dict(ptrs=dict(lse=None)), NULL),
+    ("prepare", dict(ptrs=dict(dO=P + 2)), ALIGN), ("prepare", dict(ws=None), WS),
+    ("prepare", dict(ws_bytes=8), WS),
+    ("dkdv", dict(scale=float("nan")), ARG), ("dkdv", dict(ptrs=dict(K=None)), NULL),
+    ("dkdv", dict(ptrs=dict(dV=None)), NULL), ("dkdv", dict(ptrs=dict(Q=None)), NULL),
+    ("dkdv", dict(ptrs=dict(dK=P + 8)), ALIGN), ("dkdv", dict(ws=None), WS),
+    ("dq", dict(ptrs=dict(dQ=None)), NULL), ("dq", dict(ptrs=dict(V=None)), NULL),
+    ("dq", dict(ptrs=dict(dO=None)), NULL), ("dq", dict(ptrs=dict(Q=P + 4)), ALIGN),
+    ("dq", dict(ws_bytes=0), WS), ("dq", dict(d=96), UNSUP),
+])
+def test_bwd_stages_reject(lib, name, kw, status):
+    assert _stage(lib, name, **kw) == status
+
+
+def test_bwd_stages_ignore_pointers_they_do_not_use(lib):
+    # Each stage validates only what it reads or writes: the rest may be NULL
+    # (the call is still rejected, here for a missing workspace, so nothing
+    # is launched).
+    nul = {k: None for k in ("Q", "K", "V", "dQ", "dK", "dV")}
+    assert _stage(lib, "prepare", ptrs=nul, ws=None) == WS
+    assert _stage(lib, "dkdv", ptrs=dict(O=None, lse=None, dQ=None), ws=None) == WS
+    assert _stage(lib, "dq", ptrs=dict(O=None, lse=None, dK=None, dV=None), ws=None) == WS
+
+
+def test_bwd_stages_empty_is_ok(lib):
+    nul = {k: None for k in ("Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV")}
+    for name in ("prepare", "dkdv", "dq"):
+        assert _stage(lib, name, B=0, ptrs=nul, ws=None, ws_bytes=0) == OK
+
+
 def test_bwd_empty_is_ok(lib):
     nul = {k: None for k in ("Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV")}
     assert _bwd(lib, B=0, ptrs=nul, ws=None, ws_bytes=0) == OK
@@ -113,7 +161,7 @@ def test_workspace_is_linear_in_length(lib):
     assert mem["MiB_doubled"] == mem["growth_when_L_doubles"] * mem["MiB"]  # ... the scores grow 4x
     assert mem["elements"] == L * L and mem["bytes"] == L * L * mem["bytes_per_element"]
     assert w1 < mem["bytes"] / 10                     # far below one head's score matrix
-    assert lib.fa_bwd_workspace_bytes(F32, 1, 1, L, L, 128) == L * 4
+    assert lib.fa_bwd_workspace_bytes(F32, 1, 1, L, L, 128) == 2 * L * 4
     assert lib.fa_bwd_workspace_bytes(BF16, 1, 1, L, L, 96) == 0
     for L_ in (1024, 2048, 4096, 8192):
         assert lib.fa_bwd_workspace_bytes(BF16, 1, 32, L_, L_, 128) == 32 * L_ * 8

@@ -118,3 +118,26 @@ def test_autograd_matches_direct_calls():
     ref = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), 1 / math.sqrt(128), True)
     _assert_grads((f64(qd.grad), f64(kd.grad), f64(vd.grad)), ref, BF16_GRAD_REL, "autograd")
     assert torch.equal(kd.grad, dk) and torch.equal(vd.grad, dv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stages_equal_fused_call_across_two_streams(dtype):
+    # fa_bwd_prepare, then fa_bwd_dkdv and fa_bwd_dq on two different
+    # streams, give the same bits as fa_bwd.
+    q, k, v, do = make_inputs(1, 3, 333, 333, 128, dtype, seed=12, with_dO=True)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    announce(f"bwd stages {dtype}")
+    O, lse = fa.fa_fwd(qd, kd, vd, causal=True)
+    ref = fa.fa_bwd(qd, kd, vd, O, dod, lse, causal=True)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(qd.dtype, 1, 3, 333, 333, 128), dtype=torch.uint8,
+                     device=qd.device)
+    fa.fa_bwd_prepare(O, dod, lse, 333, ws)
+    ready = torch.cuda.Event()
+    ready.record()
+    side = torch.cuda.Stream()
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        dq = fa.fa_bwd_dq(qd, kd, vd, dod, ws, causal=True)
+    dk, dv = fa.fa_bwd_dkdv(qd, kd, vd, dod, ws, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
