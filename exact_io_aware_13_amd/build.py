@@ -70,6 +70,14 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    # A kernel whose host-side instantiation the compiler dropped leaves an
+    # undefined launch stub behind; fail here rather than at load time.
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        missing = [l.split()[-1] for l in und.splitlines() if "_ZN2fa" in l]
+        if missing:
+            raise RuntimeError("libfa links with undefined internal symbols: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

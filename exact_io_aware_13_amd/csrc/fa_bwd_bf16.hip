@@ -107,6 +107,8 @@ struct KvTile {
   static constexpr int RPK = 1024 / ROWB;            // rows per 1-KiB load instruction
   static constexpr int QTB = BQ * ROWB;              // bytes per Q (or dO) tile
   static constexpr int QLOADS = QTB / 1024 / NW;     // load instructions per wave per tile
+  static constexpr int NFETCH = 2 * QLOADS + 1;      // Q, dO, row statistics
+  static_assert(QLOADS <= 4, "immediate offsets reach 3 KiB");
   // Matrix products per tile, in issue order: S and dP of query block 0
   // (interleaved over the head dimension), the same for block 1, then dV
   // and dK of block 0 and of block 1 (interleaved).
@@ -209,22 +211,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int chunk = (lane % T::CPR) ^ swz<D>(row);
     fetch_off[i] = (row * D + chunk * 8) * 2;
   }
-  auto fetch = [&](auto Bc, int t) __attribute__((always_inline)) {
+  // The tile's fetch as NFETCH load instructions per wave, issued one at a
+  // time between matrix products (unit u): the wave's Q rows, its dO rows,
+  // then one row-statistics vector (lse2 from even waves, D from odd ones;
+  // two waves write the same bytes with the same data).  Load i of a wave
+  // goes 1 KiB after load i-1 in LDS and in memory (up to the swizzled
+  // chunk, which sits in the per-lane offset), so the loads of one tensor
+  // share one LDS base and differ in the immediate offset.
+  auto fetch_unit = [&](auto Bc, int t, auto Uc) __attribute__((always_inline)) {
+    constexpr int u = decltype(Uc)::value;
     const int q0 = (qt0 + t) * T::BQ;
-#pragma unroll
-    for (int i = 0; i < T::QLOADS; ++i) {
-      const uint32_t off = (uint32_t)(q0 * T::ROWB + fetch_off[i]);
+    if constexpr (u < T::QLOADS) {
+      constexpr int i = u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (lds_void*)(qbuf(Bc) + (w * T::QLOADS + i) * 1024), 16, off, 0, 0, 0);
+          rq, (lds_void*)(qbuf(Bc) + w * T::QLOADS * 1024), 16,
+          (uint32_t)(q0 * T::ROWB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    } else if constexpr (u < 2 * T::QLOADS) {
+      constexpr int i = u - T::QLOADS;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rdo, (lds_void*)(gbuf(Bc) + (w * T::QLOADS + i) * 1024), 16, off, 0, 0, 0);
+          rdo, (lds_void*)(gbuf(Bc) + w * T::QLOADS * 1024), 16,
+          (uint32_t)(q0 * T::ROWB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    } else {
+      const uint32_t off = (uint32_t)(q0 + lane) * 4;
+      if (w & 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)ebuf(Bc), 4, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)lbuf(Bc), 4, off, 0, 0, 0);
     }
-    if (w == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)lbuf(Bc), 4,
-                                               (uint32_t)(q0 + lane) * 4, 0, 0, 0);
-    if (w == 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)ebuf(Bc), 4,
-                                               (uint32_t)(q0 + lane) * 4, 0, 0, 0);
+  };
+  auto fetch = [&](auto Bc, int t) __attribute__((always_inline)) {
+    static_for<0, T::NFETCH>([&](auto Uc) __attribute__((always_inline)) { fetch_unit(Bc, t, Uc); });
   };
 
   // ---- per-lane LDS offsets ---------------------------------------------------
@@ -288,8 +304,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const char* gb_ = gbuf(IC<BUF>{});
     const float* lb_ = lbuf(IC<BUF>{});
     const float* eb_ = ebuf(IC<BUF>{});
-
-    if (t + 1 < nrun) fetch(IC<BUF ^ 1>{}, t + 1);
 
     u32x4 afr[T::NALL];
     f32x16 s[2], dp[2];
@@ -375,6 +389,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     auto slot = [&](auto SLc) __attribute__((always_inline)) {
       constexpr int sl = decltype(SLc)::value;
       if constexpr (sl + 2 < T::NALL) read_frag(IC<sl + 2>{});
+      // Next tile's loads, one every other product early in the tile (so
+      // their issue overlaps the matrix cores).  The tile after the last one
+      // is fetched too: it reads as zeros and nothing uses it.
+      if constexpr (sl >= 2 && sl % 2 == 0 && (sl - 2) / 2 < T::NFETCH)
+        fetch_unit(IC<BUF ^ 1>{}, t + 1, IC<(sl - 2) / 2>{});
       // Row statistics of group g, two slots before the unit that needs them.
       static_for<0, 4>([&](auto Gc) __attribute__((always_inline)) {
         constexpr int g = decltype(Gc)::value;
@@ -408,11 +427,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   if (nrun > 0) {
     step(IC<0>{}, std::integral_constant<bool, CAUSAL>{}, 0);
     step(IC<1>{}, std::integral_constant<bool, CAUSAL>{}, 1);
-    for (int t = 2; t < nrun; t += 2) {
+    // Pairs of tiles with no exit between them (an exit after the first
+    // body makes the register allocator give the two bodies different
+    // accumulator registers and copy them every tile), then an odd last one.
+    int t = 2;
+    for (; t + 1 < nrun; t += 2) {
       step(IC<0>{}, std::false_type{}, t);
-      if (t + 1 >= nrun) break;
       step(IC<1>{}, std::false_type{}, t + 1);
     }
+    if (t < nrun) step(IC<0>{}, std::false_type{}, t);
   }
 
   // dK = scale * dK^T accumulator, dV = dV^T accumulator, one key row per lane.
@@ -450,6 +473,7 @@ struct DqTile {
   static constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
   static constexpr int RPK = 1024 / ROWB;
   static constexpr int LOADS = TILEB / 1024 / NW; // load instructions per wave per tile
+  static_assert(LOADS <= 4, "immediate load offsets reach 3 KiB");
   static constexpr int NFRAG = NKB * KS;          // K (= V) fragments per tile
   static constexpr int NT = (BC / 16) * DB;       // K^T fragments per tile
   // Products per iteration: S^T of tile j, dP^T of tile j, dQ^T of tile j-1.
@@ -527,17 +551,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   auto fetch = [&](int tile, auto SLc) __attribute__((always_inline)) {
     // Tiles past the last one re-fetch the last tile into a free slot, which
     // keeps the number of loads in flight the same every iteration.
+    // One LDS base per tensor; load i adds i KiB through the immediate offset.
     const int t = min(tile, nkt - 1);
-    char* kd = kslot(SLc);
-    char* vd = vslot(SLc);
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const uint32_t off = (uint32_t)(t * T::TILEB + fetch_off[i]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + (w * T::LOADS + i) * 1024), 16,
-                                               off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + (w * T::LOADS + i) * 1024), 16,
-                                               off, 0, 0, 0);
-    }
+    lds_void* kd = (lds_void*)(kslot(SLc) + w * T::LOADS * 1024);
+    lds_void* vd = (lds_void*)(vslot(SLc) + w * T::LOADS * 1024);
+    static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, kd, 16, (uint32_t)(t * T::TILEB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    });
+    static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, vd, 16, (uint32_t)(t * T::TILEB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    });
   };
 
   // ---- per-lane LDS offsets ---------------------------------------------------
@@ -760,14 +787,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
   // dS^T of even tiles goes to dskA, of odd tiles to dskB.
   iter(IC<0>{}, std::true_type{}, 0, dskB, dskA);
-  for (int j = 1; j < nkt; j += 4) {
+  // Whole rounds of four with no exit inside (an exit between bodies makes
+  // the register allocator move the accumulators around every round), then
+  // up to three more.
+  int j = 1;
+  for (; j + 3 < nkt; j += 4) {
     iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
-    if (j + 1 >= nkt) break;
     iter(IC<2>{}, std::false_type{}, j + 1, dskB, dskA);
-    if (j + 2 >= nkt) break;
     iter(IC<3>{}, std::false_type{}, j + 2, dskA, dskB);
-    if (j + 3 >= nkt) break;
     iter(IC<0>{}, std::false_type{}, j + 3, dskB, dskA);
+  }
+  if (j < nkt) {
+    iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
+    if (j + 1 < nkt) {
+      iter(IC<2>{}, std::false_type{}, j + 1, dskB, dskA);
+      if (j + 2 < nkt) iter(IC<3>{}, std::false_type{}, j + 2, dskA, dskB);
+    }
   }
 
   // ---- dQ^T of the last tile -------------------------------------------------------

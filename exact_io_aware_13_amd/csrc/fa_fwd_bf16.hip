@@ -75,6 +75,7 @@ struct FwdTile {
   static constexpr int TILEB = BC * ROWB;         // bytes per K (or V) tile
   static constexpr int RPK = 1024 / ROWB;         // rows per 1-KiB load instruction
   static constexpr int LOADS = TILEB / 1024 / NW; // load instructions per wave per tile
+  static_assert(LOADS <= 4, "immediate load offsets reach 3 KiB");
   static constexpr int NFRAG = NKB * KS;          // K fragments per tile (= V fragments)
   static_assert(NFRAG == (BC / 16) * DB, "one K and one V fragment per step");
   // Softmax slot program (both row blocks): row-max chains, running
@@ -151,12 +152,16 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
                    __attribute__((always_inline)) {
     // Tiles past the last one re-fetch the last tile into a free slot, which
     // keeps the number of loads in flight the same every iteration.
+    // Load i lands 1 KiB after load i-1 in LDS and in memory (up to the
+    // swizzled chunk, carried by the per-lane offset): one LDS base for the
+    // wave's loads, the rest in the immediate offset.
     const int t = min(tile, nkt - 1);
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i)
+    lds_void* dst = (lds_void*)(slot + w * T::LOADS * 1024);
+    static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_void*)(slot + (w * T::LOADS + i) * 1024), 16,
-          (uint32_t)(t * T::TILEB + fetch_off[i]), 0, 0, 0);
+          r, dst, 16, (uint32_t)(t * T::TILEB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    });
   };
 
   // ---- per-lane LDS read offsets (slot-relative) -----------------------------
