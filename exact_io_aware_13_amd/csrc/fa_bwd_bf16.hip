@@ -16,9 +16,10 @@
 //            matrix-product operands, dK and dV accumulate in registers
 //            over every 64-row query tile that can see the keys.
 //  3. dQ:    query-stationary, laid out like the forward.  One workgroup =
-//            4 waves x 64 query rows; K and V stream through LDS, and per
-//            key tile the wave recomputes S^T and dP^T, forms dS^T, and
-//            accumulates dQ^T = K^T dS^T in registers.
+//            256 query rows (d=128: 8 waves x 32 rows, d=64: 4 waves x 64);
+//            K and V stream through LDS, and per key tile the wave
+//            recomputes S^T and dP^T, forms dS^T, and accumulates
+//            dQ^T = K^T dS^T in registers.
 // Splitting dQ off costs two extra matrix products per (key, query) tile
 // pair (S and dP are computed by both kernels), but a fused kernel has to
 // add every dQ partial into memory with fp32 atomics, 64 x d of them per
@@ -461,8 +462,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTile {
-  static constexpr int NW = 4;                    // waves per workgroup
-  static constexpr int RB = 2;                    // 32-row blocks per wave
+  // d=128: 8 waves of one 32-row block (two waves per SIMD, each within 256
+  // registers); d=64: 4 waves of two blocks.
+  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
+  static constexpr int RB = D == 128 ? 1 : 2;     // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   static constexpr int BC = D == 128 ? 32 : 64;   // keys per tile
   static constexpr int NKB = BC / 32;             // 32-key blocks per tile
@@ -484,7 +487,7 @@ struct DqTile {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   int qt = wg_id() / BH;
   if (CAUSAL) qt = n_qt - 1 - qt;
   const int q0 = qt * T::BR;
-  const int qw0 = q0 + 64 * w;
+  const int qw0 = q0 + 32 * T::RB * w;
 
   const size_t qoff = (size_t)bh * Lq * D, koff = (size_t)bh * Lk * D;
   const auto rq = make_rsrc(Q + qoff, (uint32_t)Lq * D * 2);
@@ -624,7 +627,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   }
   // dO fragment of row block rb, step ks (B operand of dP^T).
   auto gread = [&](int rb, int ks) __attribute__((always_inline)) {
-    return lds_read16(GR, (64 * w + 32 * rb) * T::ROWB + koffs[ks]);
+    return lds_read16(GR, (32 * T::RB * w + 32 * rb) * T::ROWB + koffs[ks]);
   };
 
   f32x16 dq[T::RB][T::DB];

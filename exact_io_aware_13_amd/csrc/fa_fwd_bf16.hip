@@ -1,8 +1,9 @@
 // Exact attention forward, bf16 inputs, fp32 accumulation, gfx950.
 //
-// One workgroup = 4 waves = 256 query rows of one (batch, head) slice; each
-// wave owns 64 rows as two 32-row blocks.  The Q rows stay in registers for
-// the whole key loop; K and V stream through LDS in 64-key tiles, and an
+// One workgroup = 256 query rows of one (batch, head) slice: at d=128 8
+// waves of one 32-row block each (two waves per SIMD), at d=64 4 waves of two
+// blocks.  The Q rows stay in registers for the whole key loop; K and V
+// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, and an
 // online softmax keeps a running max m, a running sum l and an unnormalised
 // output per row, rescaling both by exp(m_old - m_new) when the max moves
 // ("How Flash Attention Improves Transformer Memory Efficiency ...",
@@ -22,7 +23,7 @@
 // element u of rows 0..3, i.e. four consecutive keys of one head-dim column).
 // O^T's accumulator again gives each lane one query row, so the rescale is a
 // per-lane scalar multiply.  Every K or V fragment read from LDS feeds the
-// products of both row blocks.
+// products of all the wave's row blocks.
 //
 // Data movement.  K and V tiles go from HBM/L2 straight into LDS with
 // bounds-checked buffer loads (rows past the end of the slice read as zero),
@@ -60,8 +61,11 @@ namespace {
 
 template <int D>
 struct FwdTile {
-  static constexpr int NW = 4;                    // waves per workgroup
-  static constexpr int RB = 2;                    // 32-row blocks per wave
+  // d=128: 8 waves of one 32-row block, two waves per SIMD (each fits in
+  // 256 registers), so one wave's softmax runs while the other's matrix
+  // products do; d=64: 4 waves of two blocks.
+  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
+  static constexpr int RB = D == 128 ? 1 : 2;     // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   // Keys per tile: at d=128 a 32-key tile keeps the softmax working set
   // (two score sets, two probability sets) inside the 256 VGPRs the vector
@@ -78,7 +82,7 @@ struct FwdTile {
   static_assert(LOADS <= 4, "immediate load offsets reach 3 KiB");
   static constexpr int NFRAG = NKB * KS;          // K fragments per tile (= V fragments)
   static_assert(NFRAG == (BC / 16) * DB, "one K and one V fragment per step");
-  // Softmax slot program (both row blocks): row-max chains, running
+  // Softmax slot program (all row blocks): row-max chains, running
   // statistics, 4-probability groups in three stages, running sums.
   static constexpr int NMAXP = 2 * NKB;           // max chains per row block (8 scores each)
   static constexpr int NGROUP = RB * 4 * NKB;     // 4-probability groups per iteration
@@ -86,14 +90,14 @@ struct FwdTile {
   static constexpr int SL_GROUPS = SL_STATS + RB;
   static constexpr int SL_SUMS = SL_GROUPS + 3 * NGROUP;
   static constexpr int NPROG = SL_SUMS + RB;      // program slots
-  static constexpr int NPHYS = 4 * NFRAG;         // matrix-product slots per iteration
+  static constexpr int NPHYS = 2 * RB * NFRAG;    // matrix-product slots per iteration
   // Program slots run after physical slot p: [prog_begin(p), prog_begin(p+1)),
   // an even spread of the program over the products.
   static constexpr int prog_begin(int p) { return (p * NPROG + NPHYS - 1) / NPHYS; }
 };
 
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign) {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
   int qt = wg_id() / BH;
   if (CAUSAL) qt = n_qt - 1 - qt;
   const int q0 = qt * T::BR;
-  const int qw0 = q0 + 64 * w;  // this wave's first row
+  const int qw0 = q0 + 32 * T::RB * w;  // this wave's first row
 
   const size_t qoff = (size_t)bh * Lq * D;
   const size_t koff = (size_t)bh * Lk * D;
@@ -218,7 +222,12 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
-  float m[T::RB] = {-INFINITY, -INFINITY}, l[T::RB] = {0.f, 0.f};
+  float m[T::RB], l[T::RB];
+#pragma unroll
+  for (int rb = 0; rb < T::RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+  }
 
   // Pipeline registers: raw scores of the current and next tile, packed bf16
   // probabilities of the previous and current tile.  Defined up front: the
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
     auto slot_work = [&](auto SLc) __attribute__((always_inline)) {
       constexpr int sl = decltype(SLc)::value;
       if constexpr (sl < T::SL_STATS) {
-        constexpr int rb = sl % 2, k = sl / 2, kb2 = k >> 1, r0 = (k & 1) * 8;
+        constexpr int rb = sl % T::RB, k = sl / T::RB, kb2 = k >> 1, r0 = (k & 1) * 8;
         const f32x16& x = s_cur[rb][kb2];
         float mm = fmaxf(fmaxf(x[r0], x[r0 + 1]), x[r0 + 2]);
         mm = fmaxf(fmaxf(mm, x[r0 + 3]), x[r0 + 4]);
@@ -361,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
         pin(base[rb]);
       } else if constexpr (sl < T::SL_SUMS) {
         constexpr int t = sl - T::SL_GROUPS, g = t / 3, stage = t % 3;
-        constexpr int rb = g & 1, eg = g >> 1, kb2 = eg >> 2, r0 = (eg & 3) * 4;
+        constexpr int rb = g % T::RB, eg = g / T::RB, kb2 = eg >> 2, r0 = (eg & 3) * 4;
         if constexpr (stage == 0) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -396,8 +405,8 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
           [&](auto SLc) __attribute__((always_inline)) { slot_work(SLc); });
     };
 
-    // NFRAG steps: score products of K fragment i (both row blocks), value
-    // products of V fragment i (both row blocks), slot work after each.
+    // NFRAG steps: score products of K fragment i (every row block), value
+    // products of V fragment i (every row block), slot work after each.
     u32x4 ka[T::NFRAG], va[T::NFRAG];
     ka[0] = kread(kb, 0);
     ka[1] = kread(kb, 1);
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
         } else {
           s_next[rb][kb2] = mma(as_bf16x8(ka[i]), qf[rb][ks], s_next[rb][kb2]);
         }
-        run_slot(IC<4 * i + rb>{});
+        run_slot(IC<2 * T::RB * i + rb>{});
         __builtin_amdgcn_sched_barrier(0);
       });
       static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
@@ -437,12 +446,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(
           bp.w = pk_prev[rb][kb2][hf * 4 + 3];
           oacc[rb][db] = mma(as_bf16x8(va[i]), as_bf16x8(bp), oacc[rb][db]);
         }
-        run_slot(IC<4 * i + 2 + rb>{});
+        run_slot(IC<2 * T::RB * i + T::RB + rb>{});
         __builtin_amdgcn_sched_barrier(0);
       });
     });
     // Rescale after P(j-1)V(j-1) is in, before P(j)V(j) is added.
-    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+    bool moved = false;
+#pragma unroll
+    for (int rb = 0; rb < T::RB; ++rb) moved |= alpha[rb] != 1.f;
+    if (__any(moved)) {
 #pragma unroll
       for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
