@@ -39,6 +39,7 @@ from workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs  # noqa: E402
 METRIC = "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B1 H32 L4096 d128 causal"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak (published)
+MIN_WARMUP_S = 0.25           # least busy time before the timed steps
 CSRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -166,9 +167,19 @@ def main():
         if ev is not None:
             ev[len(calls)].record()
 
+    # Warmup: the W steps asked for, then more untimed steps until the GPU has
+    # been busy for at least MIN_WARMUP_S, so that clocks have ramped up
+    # before the timed region whatever W is.  The extra count is reported.
+    t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(10):
+            step()
+        extra += 10
+        torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -205,6 +216,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_extra_steps": extra,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -30,10 +30,10 @@
 // no VGPR staging.  Each 16-byte chunk c of row r is stored at chunk
 // c ^ swz(r), so both the K reads (16 rows, one chunk each) and the
 // transposed V reads (4 rows x 32 bytes per 16 lanes) hit distinct banks.
-// K and V each use a 3-slot ring (one LDS array per slot, so the compiler
-// waits only for the load a read depends on); tile t's K is fetched two
-// iterations before the score product that needs it, its V two iterations
-// before the value product.
+// K and V each use a 4-slot ring (one LDS array per slot, so the compiler
+// waits only for the load a read depends on); tile t's K and V are fetched
+// three iterations before the products that need them, from inside the
+// product sequence, and each iteration ends with one wait and one barrier.
 //
 // Software pipeline.  Iteration j runs the score product of tile j+1 and the
 // value product of tile j-1 on the matrix cores while the vector ALUs run
@@ -105,18 +105,24 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char K3[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V2[T::TILEB];
+  __shared__ __attribute__((aligned(1024))) char V3[T::TILEB];
   auto kslot = [&](auto I) __attribute__((always_inline)) -> char* {
-    if constexpr (decltype(I)::value == 0) return K0;
-    else if constexpr (decltype(I)::value == 1) return K1;
-    else return K2;
+    constexpr int v = decltype(I)::value;
+    if constexpr (v == 0) return K0;
+    else if constexpr (v == 1) return K1;
+    else if constexpr (v == 2) return K2;
+    else return K3;
   };
   auto vslot = [&](auto I) __attribute__((always_inline)) -> char* {
-    if constexpr (decltype(I)::value == 0) return V0;
-    else if constexpr (decltype(I)::value == 1) return V1;
-    else return V2;
+    constexpr int v = decltype(I)::value;
+    if constexpr (v == 0) return V0;
+    else if constexpr (v == 1) return V1;
+    else if constexpr (v == 2) return V2;
+    else return V3;
   };
 
   const int tid = wi_id();
@@ -287,21 +293,20 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     }
   };
 
-  // One pipelined iteration j.  R = j mod 6 fixes the ring slots and which
+  // One pipelined iteration j.  R = j mod 4 fixes the ring slots and which
   // register set is current; FIRST (j = 0) has no previous value product.
   auto iter = [&](auto Rc, auto FIRSTc, int j, f32x16 (&s_cur)[T::RB][T::NKB],
                   f32x16 (&s_next)[T::RB][T::NKB], const unsigned (&pk_prev)[T::RB][T::NKB][8],
                   unsigned (&pk_cur)[T::RB][T::NKB][8]) __attribute__((always_inline)) {
     constexpr int R = decltype(Rc)::value;
     constexpr bool FIRST = decltype(FIRSTc)::value;
-    const char* kb = kslot(IC<(R + 1) % 3>{});
-    const char* vb = vslot(IC<(R + 2) % 3>{});
+    const char* kb = kslot(IC<(R + 1) % 4>{});  // K[j+1]
+    const char* vb = vslot(IC<(R + 3) % 4>{});  // V[j-1]
 
-    block_barrier();  // every wave is done with the slots refilled below
-    fetch(rk, j + 3, kslot(IC<R % 3>{}));
-    fetch(rv, j + 1, vslot(IC<(R + 1) % 3>{}));
-    wait_vm<4 * T::LOADS>();  // K[j+1] and V[j-1] landed: only the 2 newest iterations in flight
-    block_barrier();
+    // K[j+1] and V[j-1] were fetched three iterations ahead and waited for
+    // at the end of iteration j-1.  This iteration refills the slots of K[j]
+    // and V[j-2], whose last readers ran in iteration j-1 (closed by its
+    // barrier), with K[j+4] and V[j+2], from inside the product sequence.
 
     // Mask tile j where it crosses the causal diagonal or the end of the keys.
     const int key0 = j * T::BC;
@@ -401,6 +406,8 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     // All program slots mapped to physical slot P.
     auto run_slot = [&](auto Pc) __attribute__((always_inline)) {
       constexpr int p = decltype(Pc)::value;
+      if constexpr (p == 1) fetch(rk, j + 4, kslot(IC<R>{}));
+      if constexpr (p == 3) fetch(rv, j + 2, vslot(IC<(R + 2) % 4>{}));
       static_for<T::prog_begin(p), T::prog_begin(p + 1)>(
           [&](auto SLc) __attribute__((always_inline)) { slot_work(SLc); });
     };
@@ -462,33 +469,41 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha[rb];
     }
+    wait_vm<4 * T::LOADS>();  // loads of iteration j-2 and older landed
+    block_barrier();
   };
 
   // ---- prologue ---------------------------------------------------------------
-  // Fetch order K0, K1, K2, V0; iteration j then fetches K[j+3] and V[j+1].
+  // Issue order K0, K1, K2, V0, K3, V1 (each pair of the last four stands
+  // for an iteration that fetches K[j+4] and V[j+2], so the end-of-iteration
+  // wait covers them); iteration j then fetches K[j+4] and V[j+2].
   fetch(rk, 0, K0);
+  __builtin_amdgcn_sched_barrier(0);
   fetch(rk, 1, K1);
+  __builtin_amdgcn_sched_barrier(0);
   fetch(rk, 2, K2);
+  __builtin_amdgcn_sched_barrier(0);
   fetch(rv, 0, V0);
-  wait_vm<3 * T::LOADS>();  // K0 landed
+  __builtin_amdgcn_sched_barrier(0);
+  fetch(rk, 3, K3);
+  __builtin_amdgcn_sched_barrier(0);
+  fetch(rv, 1, V1);
+  wait_vm<4 * T::LOADS>();  // K0 and K1 landed
   block_barrier();
   score_tile(K0, sA);
+  block_barrier();  // every wave is done with K0 before iteration 0 refills its slot
 
   iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB);
-  // Six iterations per trip (j = 1..6 mod 6) as one straight-line chain, so
+  // Four iterations per trip (j = 1..4 mod 4) as one straight-line chain, so
   // ring slots and register roles are compile-time in every body.
-  for (int j = 1; j < nkt; j += 6) {
+  for (int j = 1; j < nkt; j += 4) {
     iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA);
     if (j + 1 >= nkt) break;
     iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB);
     if (j + 2 >= nkt) break;
     iter(IC<3>{}, std::false_type{}, j + 2, sB, sA, pB, pA);
     if (j + 3 >= nkt) break;
-    iter(IC<4>{}, std::false_type{}, j + 3, sA, sB, pA, pB);
-    if (j + 4 >= nkt) break;
-    iter(IC<5>{}, std::false_type{}, j + 4, sB, sA, pB, pA);
-    if (j + 5 >= nkt) break;
-    iter(IC<0>{}, std::false_type{}, j + 5, sA, sB, pA, pB);
+    iter(IC<0>{}, std::false_type{}, j + 3, sA, sB, pA, pB);
   }
 
   // Value product of the last tile: P(nkt-1) is in pB when nkt-1 is even.
@@ -496,10 +511,11 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
   block_barrier();
   {
     const unsigned(&plast)[T::RB][T::NKB][8] = ((nkt - 1) & 1) ? pA : pB;
-    switch ((nkt - 1) % 3) {
+    switch ((nkt - 1) & 3) {
       case 0: value_tile(V0, plast); break;
       case 1: value_tile(V1, plast); break;
-      default: value_tile(V2, plast); break;
+      case 2: value_tile(V2, plast); break;
+      default: value_tile(V3, plast); break;
     }
   }
 
