@@ -15,6 +15,9 @@ pages):
   shape B x H x L_q x L_k and the post-softmax matrix P that weights V.
 * "What Is FlashAttention? ...", section "The problem it solves": build the
   score matrix, apply softmax row-wise, multiply by the values.
+* The same annotated-code page, section "The Three Running Statistics":
+  results over separate key ranges combine exactly through their softmax
+  normalisers (``splitkv``: one key range, and the merge).
 * The same annotated-code page, section "Backward Pass Efficiency": the
   backward keeps per-row statistics (D_i and the softmax normaliser) instead
   of the matrices.  The gradient formulas themselves are the chain rule
@@ -32,6 +35,7 @@ from .attention import (
     attn_bwd,
     attn_bwd_heads,
 )
+from .splitkv import attn_fwd_keyrange, merge_partials
 
 __all__ = [
     "visible_mask",
@@ -39,4 +43,6 @@ __all__ = [
     "attn_fwd_rows",
     "attn_bwd",
     "attn_bwd_heads",
+    "attn_fwd_keyrange",
+    "merge_partials",
 ]

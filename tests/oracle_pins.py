@@ -300,6 +300,96 @@ def pin_bwd_heads_consistency(oracle):
             _close(a[n], f[b, h], 1e-14, "per-head backward equals full backward")
 
 
+# --------------------------------------------------------------------------
+# key-range pins (attention over one range of keys, and the merge of ranges)
+# --------------------------------------------------------------------------
+
+def _ranges(rng, Lk, n):
+    cuts = np.sort(rng.integers(0, Lk + 1, size=n - 1))
+    b = [0] + list(cuts) + [Lk]
+    return list(zip(b[:-1], b[1:]))
+
+
+def pin_keyrange_whole(oracle):
+    # The range [0, Lk) is the whole key set.
+    q, k, v = _qkv(40, 1, 2, 9, 9, 3)
+    for causal in (False, True):
+        O, lse = oracle.attn_fwd(q, k, v, 0.7, causal)
+        Or, lr = oracle.attn_fwd_keyrange(q, k, v, 0.7, causal, 0, 9)
+        _close(Or, O, 1e-14, "range [0, Lk) equals the whole")
+        _close(lr, lse, 1e-14, "range [0, Lk) lse equals the whole")
+
+
+def pin_keyrange_single_key(oracle):
+    # One key in range: every row that sees it returns its value row and
+    # lse = its score; causal rows before it see nothing (O = 0, lse = -inf).
+    q, k, v = _qkv(41, 1, 1, 6, 6, 4)
+    j = 3
+    O, lse = oracle.attn_fwd_keyrange(q, k, v, 0.9, False, j, j + 1)
+    _close(O[0, 0], np.repeat(v[0, 0, j][None], 6, axis=0), 1e-15, "single key returns V_j")
+    _close(lse[0, 0], 0.9 * (q[0, 0] @ k[0, 0, j]), 1e-14, "single key lse is its score")
+    Oc, lc = oracle.attn_fwd_keyrange(q, k, v, 0.9, True, j, j + 1)
+    assert np.all(Oc[0, 0, :j] == 0) and np.all(np.isneginf(lc[0, 0, :j])), "rows before key j"
+    _close(Oc[0, 0, j:], np.repeat(v[0, 0, j][None], 6 - j, axis=0), 1e-15, "rows from key j on")
+
+
+def pin_keyrange_causal_rows(oracle):
+    # Causal range [k0, k1) for row i is the non-causal attention over the
+    # keys k0 .. min(k1, i + 1) - 1 (absolute indices), computed here from
+    # the definition one row at a time with plain Python loops.
+    q, k, v = _qkv(42, 1, 1, 7, 9, 2)
+    k0, k1, s = 2, 6, 1.1
+    O, lse = oracle.attn_fwd_keyrange(q, k, v, s, True, k0, k1)
+    for i in range(7):
+        keys = range(k0, min(k1, i + 1))
+        if not keys:
+            assert np.isneginf(lse[0, 0, i]) and np.all(O[0, 0, i] == 0), f"row {i} sees nothing"
+            continue
+        sc = [s * sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(2)) for j in keys]
+        mx = max(sc)
+        z = sum(math.exp(x - mx) for x in sc)
+        _close(lse[0, 0, i], mx + math.log(z), 1e-14, f"row {i} lse by loops")
+        o = [sum(math.exp(x - mx) / z * v[0, 0, j, c] for x, j in zip(sc, keys)) for c in range(2)]
+        _close(O[0, 0, i], o, 1e-14, f"row {i} output by loops")
+
+
+def pin_merge_partition(oracle):
+    # Any partition of the keys into ranges (some empty, some fully masked
+    # for early causal rows) merges back to the whole: the running-statistics
+    # recurrence over finished ranges.
+    rng = _rng(43)
+    for trial in range(6):
+        Lq, Lk = int(rng.integers(1, 12)), int(rng.integers(1, 20))
+        causal = bool(trial % 2)
+        q, k, v = _qkv(44 + trial, 1, 2, Lq, Lk, 3)
+        s = float(rng.uniform(0.2, 1.5))
+        O, lse = oracle.attn_fwd(q, k, v, s, causal)
+        parts = [oracle.attn_fwd_keyrange(q, k, v, s, causal, a, b)
+                 for a, b in _ranges(rng, Lk, int(rng.integers(1, 6)))]
+        Om, lm = oracle.merge_partials(np.stack([p[0] for p in parts]),
+                                       np.stack([p[1] for p in parts]))
+        _close(Om, O, 1e-13, f"merged ranges equal the whole (trial {trial})")
+        _close(lm, lse, 1e-13, f"merged lse equals the whole (trial {trial})")
+
+
+def pin_merge_library(oracle):
+    # The merged lse is the log-sum-exp over ranges (torch.logsumexp as the
+    # library routine); merging one result with itself adds log 2 to lse and
+    # leaves O unchanged.
+    r = _rng(45)
+    Op = r.standard_normal((3, 1, 2, 5, 4))
+    lp = r.standard_normal((3, 1, 2, 5)) * 3
+    lp[1, 0, 0, 2] = -np.inf
+    O, lse = oracle.merge_partials(Op, lp)
+    _close(lse, torch.logsumexp(torch.tensor(lp), dim=0).numpy(), 1e-14, "lse is logsumexp")
+    O2, l2 = oracle.merge_partials(np.stack([Op[0], Op[0]]), np.stack([lp[0], lp[0]]))
+    _close(O2, Op[0], 1e-15, "self-merge keeps O")
+    _close(l2, lp[0] + math.log(2.0), 1e-14, "self-merge adds log 2")
+
+
+SPLITKV_PINS = [pin_keyrange_whole, pin_keyrange_single_key, pin_keyrange_causal_rows,
+                pin_merge_partition, pin_merge_library]
+
 FORWARD_PINS = [pin_golden_forward, pin_single_key, pin_causal_row0, pin_identity_values,
                 pin_constant_values, pin_zero_scale, pin_hardmax, pin_bounds,
                 pin_permutation, pin_shift, pin_blockwise_merge, pin_torch_sdpa,
@@ -307,4 +397,4 @@ FORWARD_PINS = [pin_golden_forward, pin_single_key, pin_causal_row0, pin_identit
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
                  pin_gradient_invariants, pin_constant_values_backward,
                  pin_bwd_heads_consistency]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + SPLITKV_PINS

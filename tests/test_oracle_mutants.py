@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import oracle.attention as A
+import oracle.splitkv as SK
 from tests import oracle_pins
 
 
@@ -67,6 +68,35 @@ BACKWARD_MUTANTS = {
 }
 
 _real_head_forward = A._head_forward
+_real_keyrange = SK.attn_fwd_keyrange
+_real_merge = SK.merge_partials
+
+
+def _merge_variant(weights):
+    def merge(O_parts, lse_parts):
+        lse_parts = np.asarray(lse_parts, dtype=np.float64)
+        m = lse_parts.max(axis=0)
+        lse = m + np.log(np.exp(lse_parts - m).sum(axis=0))
+        w = weights(lse_parts, lse, m)
+        return (w[..., None] * np.asarray(O_parts)).sum(axis=0), lse
+    return merge
+
+
+SPLITKV_MUTANTS = {
+    "range drops its last key": (
+        "attn_fwd_keyrange", lambda q, k, v, s, c, k0, k1: _real_keyrange(q, k, v, s, c, k0, max(k0, k1 - 1))),
+    "causal rule relative to the range start": (
+        "attn_fwd_keyrange", lambda q, k, v, s, c, k0, k1: oracle.attn_fwd(
+            np.asarray(q), np.asarray(k)[:, :, k0:k1], np.asarray(v)[:, :, k0:k1], s, c)
+        if k1 > k0 else _real_keyrange(q, k, v, s, c, k0, k1)),
+    "merge weights not normalised": ("merge_partials", _merge_variant(lambda lp, lse, m: np.exp(lp - m))),
+    "merge keeps only the largest range": (
+        "merge_partials", _merge_variant(lambda lp, lse, m: (lp == m).astype(np.float64))),
+    "merge averages ranges equally": (
+        "merge_partials", _merge_variant(lambda lp, lse, m: np.ones_like(lp) / lp.shape[0])),
+    "merged lse is the largest range's": (
+        "merge_partials", lambda O, l: (_real_merge(O, l)[0], np.asarray(l).max(axis=0))),
+}
 
 
 def _failures(pins):
@@ -98,3 +128,13 @@ def test_backward_mutant_is_caught(name, monkeypatch):
 
 def test_unmutated_oracle_passes_every_pin():
     assert _failures(oracle_pins.ALL_PINS) == []
+
+
+@pytest.mark.parametrize("name", sorted(SPLITKV_MUTANTS))
+def test_splitkv_mutant_is_caught(name, monkeypatch):
+    attr, fn = SPLITKV_MUTANTS[name]
+    monkeypatch.setattr(SK, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.SPLITKV_PINS)
+    assert failed, f"no pin caught the planted mistake: {name}"
