@@ -8,13 +8,20 @@ exposes the same calls on torch tensors:
     fa_bwd(q, k, v, o, do, lse, scale, causal) -> (dQ, dK, dV)
     fa_bwd_prepare / fa_bwd_dkdv / fa_bwd_dq     (the backward's stages)
     fa_bwd_workspace_bytes(dtype, B, H, Lq, Lk, d)
+    fa_fwd_splitkv(q, k, v, scale, causal, nsplit)  -> (O, lse), keys split
+                                                       in ranges (decode shape)
+    fa_fwd_splitkv_partial / fa_fwd_splitkv_merge     (its stages)
     attention(q, k, v, causal=False, scale=None)   (autograd)
 """
 
 from .binding import (FlashAttentionFn, attention, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
-                      fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd)
+                      fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_splitkv,
+                      fa_fwd_splitkv_default_splits, fa_fwd_splitkv_merge,
+                      fa_fwd_splitkv_partial, fa_fwd_splitkv_workspace_bytes)
 from ._lib import FaError, LIB_PATH, load as load_library
 
 __all__ = ["attention", "fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_bwd_workspace_bytes", "FlashAttentionFn",
+           "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
+           "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
+           "fa_fwd_splitkv_default_splits", "FlashAttentionFn",
            "FaError", "LIB_PATH", "load_library"]

@@ -22,7 +22,9 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_bwd_workspace_bytes", "fa_status_str", "fa_version")
+           "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
+           "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
+           "fa_fwd_splitkv_default_splits", "fa_status_str", "fa_version")
 
 _lib = None
 
@@ -53,6 +55,19 @@ def _declare(lib):
                               ctypes.c_size_t, vp]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64]
+    lib.fa_fwd_splitkv.restype = i32
+    lib.fa_fwd_splitkv.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, i64,
+                                   vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_splitkv_partial.restype = i32
+    lib.fa_fwd_splitkv_partial.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, i64,
+                                           vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_splitkv_merge.restype = i32
+    lib.fa_fwd_splitkv_merge.argtypes = [i32, i64, i64, i64, i64, i64, vp, ctypes.c_size_t, vp, vp,
+                                         vp]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
+    lib.fa_fwd_splitkv_default_splits.restype = i64
+    lib.fa_fwd_splitkv_default_splits.argtypes = [i64, i64, i64, i64, i64]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [i32]
     lib.fa_version.restype = ctypes.c_char_p

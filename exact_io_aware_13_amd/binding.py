@@ -1,7 +1,8 @@
 """Python binding of libfa with the C ABI's names.
 
 ``fa_fwd``, ``fa_bwd`` (and its stages ``fa_bwd_prepare``, ``fa_bwd_dkdv``,
-``fa_bwd_dq``) and ``fa_bwd_workspace_bytes`` only marshal torch tensors
+``fa_bwd_dq``), ``fa_bwd_workspace_bytes`` and the key-split forward
+(``fa_fwd_splitkv`` and its stages) only marshal torch tensors
 (device pointers, sizes, the current HIP stream) into the C calls;
 all arithmetic runs in the library's HIP kernels.  PyTorch supplies device
 memory and streams.  ``attention`` wraps both calls in an autograd Function
@@ -176,6 +177,87 @@ def fa_bwd_dq(q, k, v, do, workspace, scale=None, causal=False, dq=None):
                                workspace.numel(), _stream(dev))
     _lib.check(st)
     return dq
+
+
+def fa_fwd_splitkv_default_splits(B, H, Lq, Lk, d):
+    """Split count that fills the current device for these sizes."""
+    return int(_lib.load().fa_fwd_splitkv_default_splits(B, H, Lq, Lk, d))
+
+
+def fa_fwd_splitkv_workspace_bytes(dtype, B, H, Lq, Lk, d, nsplit):
+    """Bytes of workspace the key-split forward needs (0 if it would reject)."""
+    return int(_lib.load().fa_fwd_splitkv_workspace_bytes(_code(dtype), B, H, Lq, Lk, d, nsplit))
+
+
+def _splitkv_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    _check_tensor("k", k, dev, q.dtype, (B, H, Lk, d))
+    _check_tensor("v", v, dev, q.dtype, (B, H, Lk, d))
+    return B, H, Lq, Lk, d, dev
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=False, nsplit=None, out_dtype=None, out=None,
+                   lse=None, workspace=None):
+    """O, lse = attention(q, k, v) through libfa's ``fa_fwd_splitkv``.
+
+    Same operation and outputs as :func:`fa_fwd`, with the keys cut into
+    ``nsplit`` ranges (default: ``fa_fwd_splitkv_default_splits``).  bfloat16
+    inputs; ``workspace`` (uint8 device tensor) is allocated when not given.
+    """
+    B, H, Lq, Lk, d, dev = _splitkv_shapes(q, k, v)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if nsplit is None:
+        nsplit = fa_fwd_splitkv_default_splits(B, H, Lq, Lk, d)
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=out_dtype, device=dev)
+    _check_tensor("out", out, dev, out_dtype, (B, H, Lq, d))
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    if workspace is None:
+        need = fa_fwd_splitkv_workspace_bytes(q.dtype, B, H, Lq, Lk, d, nsplit)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_fwd_splitkv(_code(q.dtype), _code(out_dtype), B, H, Lq, Lk, d, _ptr(q),
+                                    _ptr(k), _ptr(v), float(scale), int(bool(causal)), int(nsplit),
+                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                    _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
+def fa_fwd_splitkv_partial(q, k, v, workspace, nsplit, scale=None, causal=False):
+    """Partial stage of the key-split forward: per-range results into
+    ``workspace`` (layout in include/fa.h)."""
+    B, H, Lq, Lk, d, dev = _splitkv_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_fwd_splitkv_partial(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k),
+                                            _ptr(v), float(scale), int(bool(causal)), int(nsplit),
+                                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+
+
+def fa_fwd_splitkv_merge(workspace, B, H, Lq, d, nsplit, out, lse):
+    """Merge stage of the key-split forward: O and lse from the per-range
+    results in ``workspace``."""
+    dev = workspace.device
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    _check_tensor("out", out, dev, None, (B, H, Lq, d))
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    st = _lib.load().fa_fwd_splitkv_merge(_code(out.dtype), B, H, Lq, d, int(nsplit),
+                                          _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                          _stream(dev))
+    _lib.check(st)
+    return out, lse
 
 
 class FlashAttentionFn(torch.autograd.Function):

@@ -3,6 +3,7 @@
 // the host and returns before any HIP call, so an invalid call enqueues
 // nothing.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -53,9 +54,9 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or too large sizes (negative size, Lk = 0 with Lq > 0, or over 2^31 bytes per slice)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension or dtype combination not implemented (d must be 64 or 128)";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer is not 16-byte aligned";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL or smaller than fa_bwd_workspace_bytes()";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL or smaller than the matching *_workspace_bytes() size";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
-    case FA_ERR_ARG: return "FA_ERR_ARG: non-finite scale or unknown enum value";
+    case FA_ERR_ARG: return "FA_ERR_ARG: non-finite scale, unknown enum value or split count out of range";
   }
   return "unknown fa_status";
 }
@@ -191,6 +192,123 @@ fa_status fa_bwd_dq(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t
                     hipStream_t stream) {
   return bwd_stages(fa::kBwdDq, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO, nullptr, scale,
                     causal, dQ, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxSplits = 4096;
+
+int64_t splitkv_chunk(int64_t Lk, int64_t nsplit) {
+  const int64_t t = fa::kSplitKvKeysPerTile;
+  return cdiv(cdiv(Lk, nsplit), t) * t;
+}
+
+// Shape and size checks of the key-split forward (sizes the merge needs
+// too: Lk is only bounded through check_shape).
+fa_status splitkv_check(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d, int64_t nsplit) {
+  if (fa_status st = check_shape(FA_BF16, B, H, Lq, Lk, d)) return st;
+  if (nsplit < 1 || nsplit > kMaxSplits) return FA_ERR_ARG;
+  const int64_t bh = B * H;
+  if (bh * cdiv(Lq, fa::kSplitKvRowsPerBlock) * nsplit > INT32_MAX) return FA_ERR_SHAPE;
+  if (cdiv(bh * Lq, 256 / (d / 4)) > INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t splitkv_opart_bytes(int64_t B, int64_t H, int64_t Lq, int64_t d, int64_t nsplit) {
+  return round_up((size_t)(nsplit * B * H * Lq * d) * sizeof(float), 256);
+}
+
+size_t splitkv_ws_bytes(int64_t B, int64_t H, int64_t Lq, int64_t d, int64_t nsplit) {
+  return splitkv_opart_bytes(B, H, Lq, d, nsplit) +
+         round_up((size_t)(nsplit * B * H * Lq) * sizeof(float), 256);
+}
+
+fa_status splitkv_run(unsigned stages, fa_dtype in_dtype, fa_dtype out_dtype, int64_t B,
+                      int64_t H, int64_t Lq, int64_t Lk, int64_t d, const void* Q, const void* K,
+                      const void* V, float scale, int causal, int64_t nsplit, void* O, float* lse,
+                      const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = splitkv_check(B, H, Lq, Lk, d, nsplit)) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (B * H * Lq == 0) return FA_OK;
+  const bool part = stages & fa::kSplitKvPartial, merge = stages & fa::kSplitKvMerge;
+  if (part && (!Q || !K || !V)) return FA_ERR_NULL;
+  if (merge && (!O || !lse)) return FA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, lse};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < splitkv_ws_bytes(B, H, Lq, d, nsplit)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  fa::SplitKvArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lse = lse;
+  a.Opart = reinterpret_cast<float*>(ws);
+  a.LSEpart = reinterpret_cast<float*>(ws + splitkv_opart_bytes(B, H, Lq, d, nsplit));
+  a.BH = (int)(B * H);
+  a.Lq = (int)Lq;
+  a.Lk = (int)Lk;
+  a.d = (int)d;
+  a.nsplit = (int)nsplit;
+  a.chunk = (int)splitkv_chunk(Lk, nsplit);
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.out_f32 = out_dtype == FA_F32;
+  const hipError_t e = fa::launch_splitkv_bf16(a, stages, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fa_fwd_splitkv_default_splits(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d) {
+  if (check_shape(FA_BF16, B, H, Lq, Lk, d) != FA_OK || B * H * Lq == 0) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int64_t blocks = B * H * cdiv(Lq, fa::kSplitKvRowsPerBlock);
+  int64_t n = cdiv(2 * (int64_t)cus, blocks);
+  n = std::min(n, std::max<int64_t>(1, Lk / 256));
+  return std::max<int64_t>(1, std::min(n, kMaxSplits));
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq,
+                                      int64_t Lk, int64_t d, int64_t nsplit) {
+  if (in_dtype != FA_BF16 || splitkv_check(B, H, Lq, Lk, d, nsplit) != FA_OK) return 0;
+  return splitkv_ws_bytes(B, H, Lq, d, nsplit);
+}
+
+fa_status fa_fwd_splitkv(fa_dtype in_dtype, fa_dtype out_dtype, int64_t B, int64_t H, int64_t Lq,
+                         int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
+                         float scale, int causal, int64_t nsplit, void* O, float* lse,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return splitkv_run(fa::kSplitKvAll, in_dtype, out_dtype, B, H, Lq, Lk, d, Q, K, V, scale, causal,
+                     nsplit, O, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_splitkv_partial(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                 int64_t d, const void* Q, const void* K, const void* V,
+                                 float scale, int causal, int64_t nsplit, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return splitkv_run(fa::kSplitKvPartial, in_dtype, FA_BF16, B, H, Lq, Lk, d, Q, K, V, scale,
+                     causal, nsplit, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype, int64_t B, int64_t H, int64_t Lq, int64_t d,
+                               int64_t nsplit, const void* workspace, size_t workspace_bytes,
+                               void* O, float* lse, hipStream_t stream) {
+  // The merge does not look at keys; one key keeps the shape checks valid.
+  return splitkv_run(fa::kSplitKvMerge, FA_BF16, out_dtype, B, H, Lq, 1, d, nullptr, nullptr,
+                     nullptr, 1.f, 0, nsplit, O, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -43,10 +43,34 @@ struct BwdArgs {
 // and are independent of each other.
 enum : unsigned { kBwdPrepare = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u };
 
+// Key-split forward (short query blocks, long key sequences).  Split s
+// covers keys [s*chunk, min((s+1)*chunk, Lk)); chunk is a multiple of
+// kSplitKvKeysPerTile.  Opart [nsplit, BH, Lq, d] and LSEpart
+// [nsplit, BH, Lq] (fp32, workspace) hold each range's normalised output and
+// natural-log lse; the merge writes O (o dtype) and lse.
+struct SplitKvArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* lse;
+  float* Opart;
+  float* LSEpart;
+  int BH, Lq, Lk, d;
+  int nsplit, chunk;
+  float scale;
+  bool causal;
+  bool out_f32;
+};
+enum : unsigned { kSplitKvPartial = 1u, kSplitKvMerge = 2u, kSplitKvAll = 3u };
+constexpr int kSplitKvKeysPerTile = 64;
+constexpr int kSplitKvRowsPerBlock = 16;
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, unsigned stages, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, unsigned stages, hipStream_t stream);
+hipError_t launch_splitkv_bf16(const SplitKvArgs& a, unsigned stages, hipStream_t stream);
 
 // Work decomposition shared by validation and the launchers.
 constexpr int kFwdBf16RowsPerBlock = 256;

@@ -71,7 +71,8 @@ typedef enum fa_status {
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned             */
   FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
   FA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch       */
-  FA_ERR_ARG = 7          /* non-finite scale or an unknown enum value         */
+  FA_ERR_ARG = 7          /* non-finite scale, an unknown enum value, or a
+                             split count outside [1, 4096]                     */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -182,6 +183,77 @@ FA_API fa_status fa_bwd_dq(fa_dtype in_dtype,
                  void* dQ,
                  const void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
+
+/*
+ * Key-split forward, for a few query rows against a long key sequence (the
+ * decode shape: generating one token attends its query to every cached key,
+ * a single pass over K and V that memory traffic bounds -- blog page "What
+ * Is FlashAttention? ...", section "What it changes for you"; explainer
+ * page "Flash attention explained", section "Why this pattern keeps
+ * recurring").  Same operation, arguments, layouts, masks and outputs as
+ * fa_fwd; the keys are cut into `nsplit` ranges processed in parallel, and
+ * the per-range results are merged exactly through their softmax
+ * normalisers (annotated-code page, section "The Three Running
+ * Statistics"):  lse = log sum_s exp(lse_s),  O = sum_s exp(lse_s - lse) O_s.
+ *
+ * Ranges.  chunk = 64 * ceil(ceil(Lk / nsplit) / 64); range s covers keys
+ * [s*chunk, min((s+1)*chunk, Lk)).  Ranges past the end of the keys are
+ * empty.  Causal masks keep their top-left meaning (absolute key and row
+ * indices).
+ *
+ * Workspace layout (fp32, written by the partial stage, read by the merge):
+ *   Opart   [nsplit, B, H, Lq, d] at byte 0: range s's output normalised by
+ *           its own softmax sum (0 for a row that sees no key of the range);
+ *   LSEpart [nsplit, B, H, Lq] at byte round_up(nsplit*B*H*Lq*d*4, 256):
+ *           range s's natural-log lse (-inf for such a row).
+ *
+ * Supported: in_dtype FA_BF16, d in {64, 128}; out_dtype FA_BF16 or FA_F32.
+ * FA_F32 inputs return FA_ERR_UNSUPPORTED (use fa_fwd).  1 <= nsplit <= 4096,
+ * else FA_ERR_ARG.  Any Lq is accepted (query rows go in blocks of 16);
+ * long query blocks are faster through fa_fwd.
+ */
+
+/* A split count that fills the current device (its compute-unit count)
+ * for these sizes: at least two workgroups per compute unit where the keys
+ * allow, with ranges of at least 256 keys.  Returns 1 for empty or invalid
+ * sizes.  Makes one HIP query of the current device. */
+FA_API int64_t fa_fwd_splitkv_default_splits(int64_t B, int64_t H, int64_t Lq,
+                 int64_t Lk, int64_t d);
+
+/* Bytes of workspace for nsplit ranges (layout above); 0 for sizes or
+ * nsplit the call would reject. */
+FA_API size_t fa_fwd_splitkv_workspace_bytes(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 int64_t nsplit);
+
+/* Partial stage then merge, on `stream`.  Arguments as for fa_fwd, plus
+ * nsplit and a 16-byte-aligned workspace of at least
+ * fa_fwd_splitkv_workspace_bytes(...) bytes (contents on entry do not
+ * matter; scratch afterwards; concurrent calls need separate workspaces). */
+FA_API fa_status fa_fwd_splitkv(fa_dtype in_dtype, fa_dtype out_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 float scale, int causal, int64_t nsplit,
+                 void* O, float* lse,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Partial stage alone: writes Opart and LSEpart into the workspace. */
+FA_API fa_status fa_fwd_splitkv_partial(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 float scale, int causal, int64_t nsplit,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Merge stage alone: reads Opart and LSEpart (for these B, H, Lq, d and
+ * nsplit) from the workspace and writes O ([B,H,Lq,d], out_dtype) and lse
+ * ([B,H,Lq] float).  Every row must have at least one finite LSEpart entry
+ * (true for anything the partial stage wrote). */
+FA_API fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t d, int64_t nsplit,
+                 const void* workspace, size_t workspace_bytes,
+                 void* O, float* lse, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 FA_API const char* fa_status_str(fa_status s);

@@ -171,3 +171,55 @@ def test_one_hip_runtime_is_mapped(lib):
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+# ---- key-split forward ------------------------------------------------------
+
+def _skv(lib, in_dt=BF16, out_dt=BF16, B=1, H=2, Lq=4, Lk=1000, d=128, Q=P, K=P, V=P,
+         scale=0.125, causal=0, nsplit=3, O=P, lse=P, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_fwd_splitkv_workspace_bytes(BF16, B, H, Lq, Lk, d, nsplit)
+    return lib.fa_fwd_splitkv(in_dt, out_dt, B, H, Lq, Lk, d, Q, K, V, scale, causal, nsplit,
+                              O, lse, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_layout(lib):
+    # Opart [nsplit,B,H,Lq,d] fp32 padded to 256 bytes, then LSEpart [nsplit,B,H,Lq].
+    def expect(B, H, Lq, d, n):
+        o = -(-(n * B * H * Lq * d * 4) // 256) * 256
+        return o + -(-(n * B * H * Lq * 4) // 256) * 256
+    for (B, H, Lq, Lk, d, n) in [(8, 32, 1, 16384, 128, 2), (1, 1, 3, 7, 64, 5), (2, 3, 17, 100, 128, 1)]:
+        assert lib.fa_fwd_splitkv_workspace_bytes(BF16, B, H, Lq, Lk, d, n) == expect(B, H, Lq, d, n)
+    assert lib.fa_fwd_splitkv_workspace_bytes(F32, 1, 1, 4, 8, 64, 2) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(BF16, 1, 1, 4, 8, 64, 0) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(BF16, 1, 1, 4, 8, 96, 2) == 0
+
+
+def test_splitkv_default_splits_in_range(lib):
+    n = lib.fa_fwd_splitkv_default_splits(8, 32, 1, 16384, 128)
+    assert 1 <= n <= 64  # at least 256 keys per range
+    assert lib.fa_fwd_splitkv_default_splits(1, 1, 1, 100, 128) == 1
+    assert lib.fa_fwd_splitkv_default_splits(0, 1, 1, 100, 128) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dt=F32, out_dt=F32), UNSUP), (dict(d=96), UNSUP), (dict(in_dt=9), ARG),
+    (dict(scale=float("nan")), ARG), (dict(nsplit=0, ws_bytes=1 << 20), ARG),
+    (dict(nsplit=4097, ws_bytes=1 << 30), ARG), (dict(Lk=0), SHAPE), (dict(B=-1), SHAPE),
+    (dict(Q=None), NULL), (dict(K=None), NULL), (dict(V=None), NULL), (dict(O=None), NULL),
+    (dict(lse=None), NULL), (dict(Q=P + 4), ALIGN), (dict(lse=P + 8), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=64), WS), (dict(ws=P + 4), ALIGN),
+    (dict(B=0), OK), (dict(Lq=0), OK),
+])
+def test_splitkv_rejects(lib, kw, status):
+    assert _skv(lib, **kw) == status
+
+
+def test_splitkv_stages_validate_their_own_pointers(lib):
+    ws = lib.fa_fwd_splitkv_workspace_bytes(BF16, 1, 2, 4, 1000, 128, 3)
+    # The partial stage takes no O/lse; the merge takes no Q/K/V.
+    assert lib.fa_fwd_splitkv_partial(BF16, 1, 2, 4, 1000, 128, None, P, P, 0.1, 0, 3, P, ws,
+                                      None) == NULL
+    assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 3, P, ws, None, P, None) == NULL
+    assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 3, P, ws - 4, P, P, None) == WS
+    assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 0, P, ws, P, P, None) == ARG

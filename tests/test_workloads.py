@@ -36,7 +36,8 @@ def test_sample_rows():
 def test_workload_table():
     assert set(WORKLOADS) == {
         "fwd_f32_B1H1L128d64", "fwd_bf16_B4H16L1024d64", "fwd_bf16_causal_B1H32L4096d128",
-        "fwd_bf16_causal_B1H8L32768d128", "bwd_bf16_causal_B2H16L2048d128"}
+        "fwd_bf16_causal_B1H8L32768d128", "bwd_bf16_causal_B2H16L2048d128",
+        "decode_bf16_B8H32Lq1Lk16384d128"}
     w = WORKLOADS["fwd_f32_B1H1L128d64"]
     q, k, v = workload_inputs(w)
     assert q.dtype == torch.float32 and q.shape == (1, 1, 128, 64)

@@ -11,7 +11,8 @@ float64, to the oracle.
 Workloads (shapes and seeds of the exact-attention study: a 4096-token
 sequence whose single-head score matrix has 16,777,216 entries, scaled to 32
 heads; a 32768-token long-context case; a short-sequence batch; a small fp32
-case; and a backward case):
+case; a backward case; and a decode case, one query row per sequence
+against a long key cache):
 """
 
 import math
@@ -59,11 +60,17 @@ WORKLOADS = {
                  (True,), 3, 1.0 / math.sqrt(128), sample_rows=256),
         Workload("bwd_bf16_causal_B2H16L2048d128", 2, 16, 2048, 2048, 128, "bf16",
                  (True,), 4, 1.0 / math.sqrt(128), backward=True),
+        # Decode: one new query row per sequence against a 16384-key cache,
+        # 8 sequences x 32 heads (the key-split forward's workload).
+        Workload("decode_bf16_B8H32Lq1Lk16384d128", 8, 32, 1, 16384, 128, "bf16",
+                 (False,), 5, 1.0 / math.sqrt(128)),
     ]
 }
 
 # The headline benchmark shape: forward + backward, causal, B1 H32 L4096 d128.
 BENCH_WORKLOAD = "fwd_bf16_causal_B1H32L4096d128"
+# The key-split forward's shape, measured beside it.
+DECODE_WORKLOAD = "decode_bf16_B8H32Lq1Lk16384d128"
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
