@@ -18,7 +18,11 @@ matrix-core peak, and -- when a counter summary for the current kernel source
 exists under profiles/ -- the HBM bytes measured by rocprofv3.  The fp64 CPU
 oracle is timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+After the timed steps, the key-split forward (fa_fwd_splitkv) is measured on
+the decode workload (B8 H32, one query row, 16384 keys, d128) and reported
+under "decode" with its HBM roofline; it is not part of "value".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
 
 import argparse
@@ -34,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import exact_io_aware_13_amd as fa  # noqa: E402
-from workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs  # noqa: E402
+from workloads import BENCH_WORKLOAD, DECODE_WORKLOAD, WORKLOADS, make_inputs  # noqa: E402
 
 METRIC = "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B1 H32 L4096 d128 causal"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak (published)
@@ -77,10 +81,10 @@ def source_hash(name):
     return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel, src):
+def measured_traffic(kernel, src, workload="B1H32L4096d128_causal"):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source; otherwise None."""
-    path = os.path.join(PROFILES, f"{kernel}_B1H32L4096d128_causal_traffic.json")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -116,12 +120,95 @@ def cpu_baseline(w, seconds_target=15.0):
                       f"{el:.1f} s wall"}
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode forward: Q, K, V read once, O and
+    lse written once."""
+    t_q = w.B * w.H * w.Lq * w.d * 2
+    t_kv = w.B * w.H * w.Lk * w.d * 2
+    return 2 * t_q + 2 * t_kv + w.B * w.H * w.Lq * 4
+
+
+def decode_cpu_baseline(w, seconds_target=3.0):
+    """The fp64 oracle on whole (batch, head) slices of the decode workload."""
+    import oracle
+    from workloads import to_f64
+    q, k, v = make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16", seed=w.seed)
+    q, k, v = (to_f64(t) for t in (q, k, v))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        b, h = divmod(n, w.H)
+        oracle.attn_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.scale,
+                        False)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target or n >= w.B * w.H:
+            break
+    per_slice = decode_bytes(w) / (w.B * w.H)
+    return {"value": round(n * per_slice / el / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+            "sample": f"{n} of {w.B * w.H} slices (fp64 numpy), {el:.1f} s wall"}
+
+
+def bench_decode(steps, warmup, with_cpu):
+    """The key-split forward on the decode workload: per-kernel HIP-event
+    times on the launching stream, HBM roofline of the whole call."""
+    w = WORKLOADS[DECODE_WORKLOAD]
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16", seed=w.seed))
+    O = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+    nsplit = fa.fa_fwd_splitkv_default_splits(w.B, w.H, w.Lq, w.Lk, w.d)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(torch.bfloat16, w.B, w.H, w.Lq, w.Lk, w.d,
+                                                       nsplit), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd_splitkv_partial(q, k, v, ws, nsplit, scale=w.scale, causal=False)
+        if ev is not None:
+            ev[1].record()
+        fa.fa_fwd_splitkv_merge(ws, w.B, w.H, w.Lq, w.d, nsplit, O, lse)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    part = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    merge = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    total = part + merge
+    nbytes = decode_bytes(w)
+    ws_bytes = nsplit * w.B * w.H * w.Lq * (w.d + 1) * 4
+    achieved = nbytes / (total * 1e-3) / 1e9
+    out = {
+        "workload": f"decode forward B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} non-causal, bf16",
+        "call": "fa_fwd_splitkv_partial + fa_fwd_splitkv_merge",
+        "nsplit": nsplit, "steps": steps, "warmup": warmup,
+        "us": round(total * 1e3, 2),
+        "kernels": {"splitkv_partial_kernel": {"us": round(part * 1e3, 2)},
+                    "splitkv_merge_kernel": {"us": round(merge * 1e3, 2)}},
+        "roofline": {"kernel": "splitkv_partial_kernel + splitkv_merge_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": nbytes, "workspace_bytes_written_and_read": ws_bytes,
+                     "traffic": measured_traffic("splitkv_partial_kernel", "fa_splitkv_bf16.hip",
+                                                 workload="decode_B8H32Lq1Lk16384d128")},
+        "cpu_baseline": decode_cpu_baseline(w) if with_cpu else None,
+    }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the key-split (decode) forward measured after the main step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -238,6 +325,9 @@ def main():
                      "algorithmic_bytes": t["bytes"]},
         "cpu_baseline": None,
     }
+    if not args.no_decode:
+        # Measured after the timed steps above; not part of value.
+        line["decode"] = bench_decode(args.steps, max(args.warmup, 20), not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
