@@ -15,10 +15,13 @@ pages):
   shape B x H x L_q x L_k and the post-softmax matrix P that weights V.
 * "What Is FlashAttention? ...", section "The problem it solves": build the
   score matrix, apply softmax row-wise, multiply by the values.
-* The same annotated-code page, section "The Three Running Statistics":
+* The annotated-code page, section "The Three Running Statistics":
   results over separate key ranges combine exactly through their softmax
   normalisers (``splitkv``: one key range, and the merge).
-* The same annotated-code page, section "Backward Pass Efficiency": the
+* Glossary page, FAQ on block-sparse extensions: a block mask removes whole
+  (query block, key block) rectangles; what remains is the same definition
+  under that mask (``blocksparse``).
+* The annotated-code page, section "Backward Pass Efficiency": the
   backward keeps per-row statistics (D_i and the softmax normaliser) instead
   of the matrices.  The gradient formulas themselves are the chain rule
   through the forward definition (the pages do not print them).
@@ -36,6 +39,7 @@ from .attention import (
     attn_bwd_heads,
 )
 from .splitkv import attn_fwd_keyrange, merge_partials
+from .blocksparse import attn_fwd_blocksparse, block_visible
 
 __all__ = [
     "visible_mask",
@@ -45,4 +49,6 @@ __all__ = [
     "attn_bwd_heads",
     "attn_fwd_keyrange",
     "merge_partials",
+    "attn_fwd_blocksparse",
+    "block_visible",
 ]

@@ -387,6 +387,74 @@ def pin_merge_library(oracle):
     _close(l2, lp[0] + math.log(2.0), 1e-14, "self-merge adds log 2")
 
 
+# --------------------------------------------------------------------------
+# block-sparse pins
+# --------------------------------------------------------------------------
+
+def pin_blocksparse_all_kept(oracle):
+    # Keeping every block is the dense attention.
+    q, k, v = _qkv(50, 1, 2, 11, 13, 3)
+    bm = np.ones((3, 4), dtype=np.uint8)
+    for causal in (False, True):
+        O, lse = oracle.attn_fwd(q, k, v, 0.6, causal)
+        Ob, lb = oracle.attn_fwd_blocksparse(q, k, v, 0.6, causal, bm, block=4)
+        _close(Ob, O, 1e-14, "all blocks kept equals dense")
+        _close(lb, lse, 1e-14, "all blocks kept: lse equals dense")
+
+
+def pin_blocksparse_block_diagonal(oracle):
+    # Keeping only the diagonal blocks is independent attention inside each
+    # block: the dense oracle on each block's own rows and keys.
+    q, k, v = _qkv(51, 1, 1, 10, 10, 3)
+    bm = np.eye(3, dtype=np.uint8)
+    O, lse = oracle.attn_fwd_blocksparse(q, k, v, 0.9, False, bm, block=4)
+    for a in range(0, 10, 4):
+        b = min(a + 4, 10)
+        Oa, la = oracle.attn_fwd(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], 0.9, False)
+        _close(O[:, :, a:b], Oa, 1e-14, f"diagonal block at {a}")
+        _close(lse[:, :, a:b], la, 1e-14, f"diagonal block lse at {a}")
+
+
+def pin_blocksparse_key_column(oracle):
+    # Keeping one key block for every row is attention over that key range.
+    q, k, v = _qkv(52, 1, 2, 9, 14, 2)
+    for causal in (False, True):
+        bm = np.zeros((3, 4), dtype=np.uint8)
+        bm[:, 1] = 1
+        O, lse = oracle.attn_fwd_blocksparse(q, k, v, 1.2, causal, bm, block=4)
+        Or, lr = oracle.attn_fwd_keyrange(q, k, v, 1.2, causal, 4, 8)
+        assert np.array_equal(np.isneginf(lse), np.isneginf(lr)), "rows that see nothing"
+        _close(O, Or, 1e-14, "one key block equals its key range")
+        f = np.isfinite(lr)
+        _close(lse[f], lr[f], 1e-14, "one key block: lse")
+
+
+def pin_blocksparse_loops(oracle):
+    # Per-element pure-Python loops on a tiny case (block 2, per-slice masks,
+    # causal), including a row that sees nothing.
+    q, k, v = _qkv(53, 1, 2, 5, 6, 2)
+    bm = np.array([[[1, 0, 1], [0, 1, 0], [1, 1, 0]],
+                   [[0, 1, 1], [1, 0, 1], [0, 0, 1]]], dtype=np.uint8)[None]
+    s = 0.7
+    O, lse = oracle.attn_fwd_blocksparse(q, k, v, s, True, bm, block=2)
+    for h in range(2):
+        for i in range(5):
+            keys = [j for j in range(6) if bm[0, h, i // 2, j // 2] and j <= i]
+            if not keys:
+                assert np.isneginf(lse[0, h, i]) and np.all(O[0, h, i] == 0), f"h{h} row {i} empty"
+                continue
+            sc = [s * sum(q[0, h, i, c] * k[0, h, j, c] for c in range(2)) for j in keys]
+            mx = max(sc)
+            z = sum(math.exp(x - mx) for x in sc)
+            _close(lse[0, h, i], mx + math.log(z), 1e-14, f"h{h} row {i} lse by loops")
+            o = [sum(math.exp(x - mx) / z * v[0, h, j, c] for x, j in zip(sc, keys)) for c in range(2)]
+            _close(O[0, h, i], o, 1e-14, f"h{h} row {i} output by loops")
+    assert np.isneginf(lse[0, 1, 0]), "row 0 of head 1 sees no key (block 0,0 dropped)"
+
+
+BLOCKSPARSE_PINS = [pin_blocksparse_all_kept, pin_blocksparse_block_diagonal,
+                    pin_blocksparse_key_column, pin_blocksparse_loops]
+
 SPLITKV_PINS = [pin_keyrange_whole, pin_keyrange_single_key, pin_keyrange_causal_rows,
                 pin_merge_partition, pin_merge_library]
 
@@ -397,4 +465,4 @@ FORWARD_PINS = [pin_golden_forward, pin_single_key, pin_causal_row0, pin_identit
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_torch_autograd,
                  pin_gradient_invariants, pin_constant_values_backward,
                  pin_bwd_heads_consistency]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + SPLITKV_PINS
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + SPLITKV_PINS + BLOCKSPARSE_PINS

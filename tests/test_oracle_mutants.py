@@ -10,6 +10,7 @@ import pytest
 import oracle
 import oracle.attention as A
 import oracle.splitkv as SK
+import oracle.blocksparse as BS
 from tests import oracle_pins
 
 
@@ -82,6 +83,38 @@ def _merge_variant(weights):
     return merge
 
 
+_real_block_visible = BS.block_visible
+
+
+def _vis_variant(change):
+    def block_visible(block_mask, Lq, Lk, block, causal):
+        bm = np.asarray(block_mask) != 0
+        rows, cols = change(np.arange(Lq), np.arange(Lk), block)
+        rows = np.clip(rows, 0, bm.shape[0] - 1)
+        cols = np.clip(cols, 0, bm.shape[1] - 1)
+        return bm[rows[:, None], cols[None, :]] & A.visible_mask(Lq, Lk, causal)
+    return block_visible
+
+
+def _transposed_visible(block_mask, Lq, Lk, block, causal):
+    # Entry (i, j) taken from block_mask[j // block, i // block].
+    bm = np.asarray(block_mask) != 0
+    r = np.clip(np.arange(Lk) // block, 0, bm.shape[0] - 1)
+    c = np.clip(np.arange(Lq) // block, 0, bm.shape[1] - 1)
+    return bm[r[None, :], c[:, None]] & A.visible_mask(Lq, Lk, causal)
+
+
+BLOCKSPARSE_MUTANTS = {
+    "block mask read transposed": ("block_visible", _transposed_visible),
+    "block index off by one row": ("block_visible", _vis_variant(lambda i, j, b: ((i + 1) // b, j // b))),
+    "block index from the key end": ("block_visible", _vis_variant(lambda i, j, b: (i // b, (j + b - 1) // b))),
+    "causal rule ignored": (
+        "block_visible", lambda bm, Lq, Lk, b, c: _real_block_visible(bm, Lq, Lk, b, False)),
+    "mask ignored": (
+        "block_visible", lambda bm, Lq, Lk, b, c: A.visible_mask(Lq, Lk, c)),
+}
+
+
 SPLITKV_MUTANTS = {
     "range drops its last key": (
         "attn_fwd_keyrange", lambda q, k, v, s, c, k0, k1: _real_keyrange(q, k, v, s, c, k0, max(k0, k1 - 1))),
@@ -137,4 +170,13 @@ def test_splitkv_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(oracle, attr, fn)
     with np.errstate(all="ignore"):
         failed = _failures(oracle_pins.SPLITKV_PINS)
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(BLOCKSPARSE_MUTANTS))
+def test_blocksparse_mutant_is_caught(name, monkeypatch):
+    attr, fn = BLOCKSPARSE_MUTANTS[name]
+    monkeypatch.setattr(BS, attr, fn)
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.BLOCKSPARSE_PINS)
     assert failed, f"no pin caught the planted mistake: {name}"
