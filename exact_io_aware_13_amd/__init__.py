@@ -5,6 +5,8 @@ behind the C ABI declared in include/fa.h).  This package loads it and
 exposes the same calls on torch tensors:
 
     fa_fwd(q, k, v, scale, causal)            -> (O, lse)
+    fa_fwd_blocksparse(q, k, v, block_mask, scale, causal) -> (O, lse),
+                                                 128x128 blocks removed
     fa_bwd(q, k, v, o, do, lse, scale, causal) -> (dQ, dK, dV)
     fa_bwd_prepare / fa_bwd_dkdv / fa_bwd_dq     (the backward's stages)
     fa_bwd_workspace_bytes(dtype, B, H, Lq, Lk, d)
@@ -15,12 +17,13 @@ exposes the same calls on torch tensors:
 """
 
 from .binding import (FlashAttentionFn, attention, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
-                      fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_splitkv,
+                      fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_blocksparse,
+                      fa_fwd_splitkv, SPARSE_BLOCK,
                       fa_fwd_splitkv_default_splits, fa_fwd_splitkv_merge,
                       fa_fwd_splitkv_partial, fa_fwd_splitkv_workspace_bytes)
 from ._lib import FaError, LIB_PATH, load as load_library
 
-__all__ = ["attention", "fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+__all__ = ["attention", "fa_fwd", "fa_fwd_blocksparse", "SPARSE_BLOCK", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_default_splits", "FlashAttentionFn",

@@ -21,7 +21,7 @@ STATUS_NAMES = {
     4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG",
 }
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_default_splits", "fa_status_str", "fa_version")
@@ -42,6 +42,9 @@ def _declare(lib):
     i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     lib.fa_fwd.restype = i32
     lib.fa_fwd.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, vp, vp, vp]
+    lib.fa_fwd_blocksparse.restype = i32
+    lib.fa_fwd_blocksparse.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, vp,
+                                       i64, vp, vp, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
                            vp, vp, vp, vp, ctypes.c_size_t, vp]

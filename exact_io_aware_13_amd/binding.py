@@ -1,6 +1,6 @@
 """Python binding of libfa with the C ABI's names.
 
-``fa_fwd``, ``fa_bwd`` (and its stages ``fa_bwd_prepare``, ``fa_bwd_dkdv``,
+``fa_fwd``, ``fa_fwd_blocksparse``, ``fa_bwd`` (and its stages ``fa_bwd_prepare``, ``fa_bwd_dkdv``,
 ``fa_bwd_dq``), ``fa_bwd_workspace_bytes`` and the key-split forward
 (``fa_fwd_splitkv`` and its stages) only marshal torch tensors
 (device pointers, sizes, the current HIP stream) into the C calls;
@@ -76,6 +76,53 @@ def fa_fwd(q, k, v, scale=None, causal=False, out_dtype=None, out=None, lse=None
     lib = _lib.load()
     st = lib.fa_fwd(_code(q.dtype), _code(out_dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
                     float(scale), int(bool(causal)), _ptr(out), _ptr(lse), _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
+SPARSE_BLOCK = 128  # query and key block edge of the block-sparse mask
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out_dtype=None, out=None,
+                       lse=None):
+    """O, lse through libfa's ``fa_fwd_blocksparse``.
+
+    ``block_mask``: uint8 (or bool) device tensor [ceil(Lq/128), ceil(Lk/128)]
+    shared by every slice, or [B, H, ceil(Lq/128), ceil(Lk/128)]; nonzero
+    keeps a 128 x 128 (query, key) block.  Rows that see no key return O = 0
+    and lse = -inf.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    _check_tensor("k", k, dev, q.dtype, (B, H, Lk, d))
+    _check_tensor("v", v, dev, q.dtype, (B, H, Lk, d))
+    nqb, nkb = -(-Lq // SPARSE_BLOCK), -(-Lk // SPARSE_BLOCK)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    if tuple(block_mask.shape) == (nqb, nkb):
+        slices = 1
+    elif tuple(block_mask.shape) == (B, H, nqb, nkb):
+        slices = B * H
+    else:
+        raise ValueError(f"block_mask must be [{nqb}, {nkb}] or [{B}, {H}, {nqb}, {nkb}]")
+    _check_tensor("block_mask", block_mask, dev, torch.uint8)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=out_dtype, device=dev)
+    _check_tensor("out", out, dev, out_dtype, (B, H, Lq, d))
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    st = _lib.load().fa_fwd_blocksparse(_code(q.dtype), _code(out_dtype), B, H, Lq, Lk, d,
+                                        _ptr(q), _ptr(k), _ptr(v), float(scale), int(bool(causal)),
+                                        _ptr(block_mask), slices, _ptr(out), _ptr(lse),
+                                        _stream(dev))
     _lib.check(st)
     return out, lse
 

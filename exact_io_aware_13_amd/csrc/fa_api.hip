@@ -91,6 +91,43 @@ fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype, int64_t B, int64_t H, in
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_blocksparse(fa_dtype in_dtype, fa_dtype out_dtype, int64_t B, int64_t H,
+                             int64_t Lq, int64_t Lk, int64_t d, const void* Q, const void* K,
+                             const void* V, float scale, int causal, const uint8_t* block_mask,
+                             int64_t mask_slices, void* O, float* lse, hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (mask_slices != 1 && mask_slices != B * H) return FA_ERR_ARG;
+  const int64_t nqb = cdiv(Lq, fa::kSparseBlock), nkb = cdiv(Lk, fa::kSparseBlock);
+  if (nkb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
+  if (nqb * nkb > INT32_MAX) return FA_ERR_SHAPE;
+  if (B * H * Lq == 0) return FA_OK;
+  if (!Q || !K || !V || !O || !lse || !block_mask) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+
+  fa::FwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lse = lse;
+  a.BH = (int)(B * H);
+  a.Lq = (int)Lq;
+  a.Lk = (int)Lk;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.out_f32 = out_dtype == FA_F32;
+  a.block_mask = block_mask;
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  a.bm_stride = mask_slices == 1 ? 0 : (int)(nqb * nkb);
+  const hipError_t e = fa::launch_fwd_bf16(a, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                               int64_t d) {
   if (!valid_dtype(in_dtype) || check_shape(in_dtype, B, H, Lq, Lk, d) != FA_OK) return 0;

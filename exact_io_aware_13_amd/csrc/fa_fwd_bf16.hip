@@ -51,6 +51,18 @@
 // the fp32 probabilities; the value product takes them rounded to bf16.
 // Tiles that are fully masked for some rows (causal diagonal band) are still
 // multiplied; their probabilities are exactly 0.
+//
+// Block-sparse instantiation (SPARSE).  A mask over 128x128 (query, key)
+// blocks removes whole blocks from the attention pattern, a generalisation
+// of the causal tile skip (the glossary page, FAQ on block-sparse
+// extensions, sets such patterns apart from the dense core).  The workgroup
+// first compacts the key blocks that either of its two 128-row blocks sees
+// into an LDS list (ballot + prefix count per wave) and then runs the same
+// pipeline over the listed key tiles only; a wave whose own row block does
+// not see a listed block masks that tile to -inf like a causal tile.  Rows
+// may see no key at all: the running max then stays -inf (the reference is
+// taken as 0 so every probability is exactly 0) and the row's output is 0
+// with lse = -inf.
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -96,11 +108,12 @@ struct FwdTile {
   static constexpr int prog_begin(int p) { return (p * NPROG + NPHYS - 1) / NPHYS; }
 };
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
 __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
-    int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign) {
+    int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign,
+    const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = FwdTile<D>;
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
@@ -148,6 +161,55 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
   int nkt = (Lk + T::BC - 1) / T::BC;
   if (CAUSAL) nkt = min(nkt, (q0 + T::BR - 1) / T::BC + 1);
 
+  // ---- block-sparse: compacted list of the key blocks this workgroup sees --
+  // Entry e: key block index in bits 0..13, bit 14 + b set if row block b
+  // of the workgroup (rows q0 + 128 b ..) sees it.
+  constexpr int TPB = kSparseBlock / T::BC;  // key tiles per mask block
+  static_assert(T::BR == 2 * kSparseBlock, "two mask row blocks per workgroup");
+  __shared__ uint16_t tlist[SPARSE ? kSparseMaxKeyBlocks : 1];
+  __shared__ int wtot[SPARSE ? T::NW : 1];
+  const int wq = (32 * T::RB * w) / kSparseBlock;  // this wave's row block
+  if constexpr (SPARSE) {
+    const int qb0 = q0 / kSparseBlock;
+    const bool has1 = qb0 + 1 < nqb;
+    const uint8_t* row0 = BM + (size_t)bh * bm_stride + (size_t)qb0 * nkb;
+    const uint8_t* row1 = row0 + nkb;
+    const int kb_lim = CAUSAL ? min(nkb, (q0 + T::BR - 1) / kSparseBlock + 1) : nkb;
+    int count = 0;
+    for (int base = 0; base < kb_lim; base += 64 * T::NW) {
+      const int kb = base + tid;
+      const bool in = kb < kb_lim;
+      const bool f0 = in && row0[kb] != 0;
+      const bool f1 = in && has1 && row1[kb] != 0;
+      const uint64_t bal = __ballot(f0 || f1);
+      const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
+      if (lane == 0) wtot[w] = __popcll(bal);
+      __syncthreads();
+      int off = count, tot = 0;
+      for (int ww = 0; ww < T::NW; ++ww) {
+        if (ww < w) off += wtot[ww];
+        tot += wtot[ww];
+      }
+      if (f0 || f1) tlist[off + below] = (uint16_t)(kb | (int(f0) << 14) | (int(f1) << 15));
+      count += tot;
+      __syncthreads();
+    }
+    nkt = count * TPB;
+  }
+  // Key tile of loop position j, and whether this wave's rows see its block.
+  auto tile_at = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE)
+      return (__builtin_amdgcn_readfirstlane(tlist[j / TPB]) & 0x3fff) * TPB + j % TPB;
+    else
+      return j;
+  };
+  auto own_sees = [&](int j) __attribute__((always_inline)) -> bool {
+    if constexpr (SPARSE)
+      return (__builtin_amdgcn_readfirstlane(tlist[j / TPB]) >> (14 + wq)) & 1;
+    else
+      return true;
+  };
+
   // ---- tile fetch: each wave moves LOADS KiB of the K (or V) tile ----------
   // Lane l of load i writes LDS bytes [16 l, 16 l + 16) of KiB (w*LOADS + i)
   // of the slot; it fetches the logical chunk that the swizzle puts there.
@@ -165,7 +227,7 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     // Load i lands 1 KiB after load i-1 in LDS and in memory (up to the
     // swizzled chunk, carried by the per-lane offset): one LDS base for the
     // wave's loads, the rest in the immediate offset.
-    const int t = min(tile, nkt - 1);
+    const int t = tile_at(min(tile, nkt - 1));
     lds_void* dst = (lds_void*)(slot + w * T::LOADS * 1024);
     static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
@@ -308,9 +370,11 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     // and V[j-2], whose last readers ran in iteration j-1 (closed by its
     // barrier), with K[j+4] and V[j+2], from inside the product sequence.
 
-    // Mask tile j where it crosses the causal diagonal or the end of the keys.
-    const int key0 = j * T::BC;
-    if ((key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > qw0)) {
+    // Mask tile j where it crosses the causal diagonal or the end of the keys
+    // (block-sparse: or where this wave's row block does not see its block).
+    const int key0 = tile_at(j) * T::BC;
+    const bool sees = own_sees(j);
+    if ((key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > qw0) || !sees) {
       // Register r of key block kb2 holds key key0 + 4h + (kb2*32 + 8(r/4) + r%4);
       // it is visible iff that constant offset is <= lim.  The sign of
       // (lim - offset) selects -inf without compares.
@@ -318,7 +382,7 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
         constexpr int rb = decltype(RBc)::value;
         const int qrow = qw0 + 32 * rb + n;
         const int last = CAUSAL ? min(Lk - 1, qrow) : Lk - 1;
-        const int lim = last - key0 - 4 * h;
+        const int lim = sees ? last - key0 - 4 * h : -(1 << 30);
         static_for<0, 16 * T::NKB>([&](auto Ec) __attribute__((always_inline)) {
           constexpr int e = decltype(Ec)::value, kb2 = e >> 4, r = e & 15;
           constexpr int off = kb2 * 32 + 8 * (r >> 2) + (r & 3);
@@ -366,11 +430,14 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
         mx = halves_max(mx);
         const float mt = mx * c;  // -inf stays -inf (c > 0)
         const float m_new = (mt > m[rb] + 8.f) ? mt : m[rb];
-        // Tile 0 holds key 0 for every row, so m_new is finite from the
-        // first tile on; exp2(0) = 1 exactly when the reference stays.
-        alpha[rb] = fast_exp2(m[rb] - m_new);
+        // Dense: tile 0 holds key 0 for every row, so m_new is finite from
+        // the first tile on; exp2(0) = 1 exactly when the reference stays.
+        // Block-sparse: a row may have seen nothing yet (m_new = -inf); the
+        // reference is then 0, so p = exp2(-inf) = 0 and alpha = 0.
+        const float ref = (SPARSE && m_new == -INFINITY) ? 0.f : m_new;
+        alpha[rb] = fast_exp2(m[rb] - ref);
         m[rb] = m_new;
-        base[rb] = m_new;
+        base[rb] = ref;
         pin(alpha[rb]);
         pin(base[rb]);
       } else if constexpr (sl < T::SL_SUMS) {
@@ -473,6 +540,9 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     block_barrier();
   };
 
+  // A block-sparse workgroup whose rows see no key skips the pipeline: its
+  // outputs are 0 and its lse -inf (the epilogue handles l = 0).
+  if (!SPARSE || nkt > 0) {
   // ---- prologue ---------------------------------------------------------------
   // Issue order K0, K1, K2, V0, K3, V1 (each pair of the last four stands
   // for an iteration that fetches K[j+4] and V[j+2], so the end-of-iteration
@@ -518,13 +588,15 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
       default: value_tile(V3, plast); break;
     }
   }
+  }  // !SPARSE || nkt > 0
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) * ln 2 ---------------------
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb) {
     const int qg = qw0 + 32 * rb + n;
     const float lt = halves_sum(l[rb]);
-    const float inv = 1.f / lt;
+    // l = 0 only for block-sparse rows that see no key: O = 0, lse = -inf.
+    const float inv = (SPARSE && lt == 0.f) ? 0.f : 1.f / lt;
     if (OUT_F32) {
       const auto ro = make_rsrc(static_cast<float*>(O) + qoff, (uint32_t)Lq * D * 4);
 #pragma unroll
@@ -550,11 +622,13 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
           store8(ro, (uint32_t)(qg * D + db * 32 + 8 * g4 + 4 * h) * 2, v);
         }
     }
-    if (h == 0 && qg < Lq) LSE[(size_t)bh * Lq + qg] = (m[rb] + __log2f(lt)) * kLn2;
+    if (h == 0 && qg < Lq)
+      LSE[(size_t)bh * Lq + qg] =
+          (SPARSE && lt == 0.f) ? -INFINITY : (m[rb] + __log2f(lt)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   using T = FwdTile<D>;
   const int n_qt = (a.Lq + T::BR - 1) / T::BR;
@@ -564,25 +638,26 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   float c = fabsf(a.scale) * kLog2e;
   if (c < 1e-30f) c = 1e-30f;
   const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32>), grid, dim3(64 * T::NW), 0, stream,
-                     static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, SPARSE>), grid, dim3(64 * T::NW), 0,
+                     stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                      static_cast<const uint16_t*>(a.V), a.O, a.lse, a.BH, a.Lq, a.Lk, n_qt, c,
-                     qsign);
+                     qsign, a.block_mask, a.bm_stride, a.nqb, a.nkb);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool SPARSE>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  if (a.causal) return a.out_f32 ? launch<D, true, true>(a, stream) : launch<D, true, false>(a, stream);
-  return a.out_f32 ? launch<D, false, true>(a, stream) : launch<D, false, false>(a, stream);
+  if (a.causal)
+    return a.out_f32 ? launch<D, true, true, SPARSE>(a, stream) : launch<D, true, false, SPARSE>(a, stream);
+  return a.out_f32 ? launch<D, false, true, SPARSE>(a, stream) : launch<D, false, false, SPARSE>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   static_assert(FwdTile<128>::BR == kFwdBf16RowsPerBlock, "tile table out of sync");
-  if (a.d == 64) return launch_d<64>(a, stream);
-  return launch_d<128>(a, stream);
+  if (a.block_mask) return a.d == 64 ? launch_d<64, true>(a, stream) : launch_d<128, true>(a, stream);
+  return a.d == 64 ? launch_d<64, false>(a, stream) : launch_d<128, false>(a, stream);
 }
 
 }  // namespace fa

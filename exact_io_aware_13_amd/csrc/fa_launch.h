@@ -18,7 +18,15 @@ struct FwdArgs {
   float scale;
   bool causal;
   bool out_f32;
+  // Block-sparse forward (bf16 only): NULL for the dense forward.  Mask
+  // [mask slices][nqb][nkb] of kSparseBlock x kSparseBlock (query, key)
+  // blocks, nonzero = visible; bm_stride = nqb*nkb per slice, or 0 when one
+  // mask serves every slice.
+  const uint8_t* block_mask = nullptr;
+  int bm_stride = 0, nqb = 0, nkb = 0;
 };
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxKeyBlocks = 4096;
 
 struct BwdArgs {
   const void* Q;

@@ -103,6 +103,32 @@ FA_API fa_status fa_fwd(fa_dtype in_dtype, fa_dtype out_dtype,
                  void* O, float* lse, hipStream_t stream);
 
 /*
+ * Block-sparse forward: fa_fwd with whole 128 x 128 (query, key) blocks
+ * removed from the attention pattern by a block mask, a generalisation of
+ * the causal tile skip (glossary page "Flash Attention", FAQ on block-sparse
+ * extensions: such a pattern is a different attention, kept apart from the
+ * dense exact core; it is still computed exactly over what it keeps).
+ *   block_mask   uint8 [mask_slices, ceil(Lq/128), ceil(Lk/128)] device
+ *                memory (any alignment): entry [s][qb][kb] nonzero means
+ *                queries 128 qb .. 128 qb + 127 of slice s may see keys
+ *                128 kb .. 128 kb + 127.
+ *   mask_slices  1 (one mask for every slice) or B*H (one per slice, in
+ *                slice order b*H + h); other values are FA_ERR_ARG.
+ * Element (i, j) of a slice is visible iff its block entry is nonzero and,
+ * with `causal`, j <= i.  Softmax, O and lse are over the visible keys only;
+ * a row that sees no key gets O = 0 and lse = -inf.  Other arguments,
+ * layouts and status codes as for fa_fwd.  Supported: in_dtype FA_BF16, d in
+ * {64, 128}, ceil(Lk/128) <= 4096 (else FA_ERR_UNSUPPORTED).  Work and time
+ * scale with the visible blocks.
+ */
+FA_API fa_status fa_fwd_blocksparse(fa_dtype in_dtype, fa_dtype out_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 float scale, int causal,
+                 const uint8_t* block_mask, int64_t mask_slices,
+                 void* O, float* lse, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs for these sizes: the D statistic
  * and lse in base 2 ([B,H,Lq] float each, each padded to a multiple of 256
  * bytes).  Linear in Lq; independent of the number of scores.  Returns 0

@@ -223,3 +223,27 @@ def test_splitkv_stages_validate_their_own_pointers(lib):
     assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 3, P, ws, None, P, None) == NULL
     assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 3, P, ws - 4, P, P, None) == WS
     assert lib.fa_fwd_splitkv_merge(BF16, 1, 2, 4, 128, 0, P, ws, P, P, None) == ARG
+
+
+# ---- block-sparse forward -----------------------------------------------------
+
+def _bs(lib, in_dt=BF16, out_dt=BF16, B=1, H=2, Lq=300, Lk=500, d=128, Q=P, K=P, V=P,
+        scale=0.125, causal=0, mask=P + 1, slices=1, O=P, lse=P):
+    return lib.fa_fwd_blocksparse(in_dt, out_dt, B, H, Lq, Lk, d, Q, K, V, scale, causal, mask,
+                                  slices, O, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dt=F32, out_dt=F32), UNSUP), (dict(d=96), UNSUP), (dict(Lk=4096 * 128 + 1), UNSUP),
+    (dict(slices=3), ARG), (dict(slices=0), ARG), (dict(scale=float("nan")), ARG),
+    (dict(Lk=0), SHAPE), (dict(mask=None), NULL), (dict(Q=None), NULL), (dict(lse=None), NULL),
+    (dict(Q=P + 4), ALIGN), (dict(O=P + 2), ALIGN), (dict(B=0), OK), (dict(Lq=0), OK),
+])
+def test_blocksparse_rejects(lib, kw, status):
+    # The mask itself may have any alignment (P + 1 above is accepted).
+    assert _bs(lib, **kw) == status
+
+
+def test_blocksparse_accepts_per_slice_mask_count(lib):
+    assert _bs(lib, B=2, H=3, slices=6, Lq=0) == OK
+    assert _bs(lib, B=2, H=3, slices=5, Lq=0) == ARG
