@@ -101,7 +101,7 @@ fa_status fa_fwd_blocksparse(fa_dtype in_dtype, fa_dtype out_dtype, int64_t B, i
   if (mask_slices != 1 && mask_slices != B * H) return FA_ERR_ARG;
   const int64_t nqb = cdiv(Lq, fa::kSparseBlock), nkb = cdiv(Lk, fa::kSparseBlock);
   if (nkb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
-  if (nqb * nkb > INT32_MAX) return FA_ERR_SHAPE;
+  if (nqb * nkb > INT32_MAX || B * H * nqb > INT32_MAX) return FA_ERR_SHAPE;  // mask, grid
   if (B * H * Lq == 0) return FA_OK;
   if (!Q || !K || !V || !O || !lse || !block_mask) return FA_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(lse))

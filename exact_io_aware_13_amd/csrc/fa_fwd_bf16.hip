@@ -55,14 +55,14 @@
 // Block-sparse instantiation (SPARSE).  A mask over 128x128 (query, key)
 // blocks removes whole blocks from the attention pattern, a generalisation
 // of the causal tile skip (the glossary page, FAQ on block-sparse
-// extensions, sets such patterns apart from the dense core).  The workgroup
-// first compacts the key blocks that either of its two 128-row blocks sees
-// into an LDS list (ballot + prefix count per wave) and then runs the same
-// pipeline over the listed key tiles only; a wave whose own row block does
-// not see a listed block masks that tile to -inf like a causal tile.  Rows
-// may see no key at all: the running max then stays -inf (the reference is
-// taken as 0 so every probability is exactly 0) and the row's output is 0
-// with lse = -inf.
+// extensions, sets such patterns apart from the dense core).  A workgroup
+// then holds 128 rows (half the waves), exactly one row block of the mask:
+// it first compacts the key blocks its row block sees into an LDS list
+// (ballot + prefix count per wave) and then runs the same pipeline over the
+// listed key tiles only.  A workgroup whose list is empty writes O = 0 and
+// lse = -inf; the softmax also tolerates a row that has seen no key yet (the
+// running max is then -inf and the reference is taken as 0, so every
+// probability is exactly 0).
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -71,12 +71,14 @@
 namespace fa {
 namespace {
 
-template <int D>
+template <int D, bool SPARSE>
 struct FwdTile {
   // d=128: 8 waves of one 32-row block, two waves per SIMD (each fits in
   // 256 registers), so one wave's softmax runs while the other's matrix
-  // products do; d=64: 4 waves of two blocks.
-  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
+  // products do; d=64: 4 waves of two blocks.  Block-sparse: half the waves,
+  // so that a workgroup's 128 rows are exactly one row block of the mask
+  // (two workgroups share a compute unit).
+  static constexpr int NW = (D == 128 ? 8 : 4) / (SPARSE ? 2 : 1);  // waves per workgroup
   static constexpr int RB = D == 128 ? 1 : 2;     // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   // Keys per tile: at d=128 a 32-key tile keeps the softmax working set
@@ -109,12 +111,12 @@ struct FwdTile {
 };
 
 template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__((64 * FwdTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, SPARSE>;
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
@@ -162,52 +164,64 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
   if (CAUSAL) nkt = min(nkt, (q0 + T::BR - 1) / T::BC + 1);
 
   // ---- block-sparse: compacted list of the key blocks this workgroup sees --
-  // Entry e: key block index in bits 0..13, bit 14 + b set if row block b
-  // of the workgroup (rows q0 + 128 b ..) sees it.
+  // The workgroup's 128 rows are one row block of the mask; its nonzero
+  // entries (up to the causal limit) are compacted in order into LDS, then
+  // held 128 at a time in two registers (entry e of the window in lane e % 64
+  // of win0 or win1) and read with v_readlane, so the loop never waits on
+  // LDS for a tile index.
   constexpr int TPB = kSparseBlock / T::BC;  // key tiles per mask block
-  static_assert(T::BR == 2 * kSparseBlock, "two mask row blocks per workgroup");
   __shared__ uint16_t tlist[SPARSE ? kSparseMaxKeyBlocks : 1];
   __shared__ int wtot[SPARSE ? T::NW : 1];
-  const int wq = (32 * T::RB * w) / kSparseBlock;  // this wave's row block
+  int nlist = 0, wbase = 0;
+  unsigned win0 = 0, win1 = 0;
   if constexpr (SPARSE) {
-    const int qb0 = q0 / kSparseBlock;
-    const bool has1 = qb0 + 1 < nqb;
-    const uint8_t* row0 = BM + (size_t)bh * bm_stride + (size_t)qb0 * nkb;
-    const uint8_t* row1 = row0 + nkb;
-    const int kb_lim = CAUSAL ? min(nkb, (q0 + T::BR - 1) / kSparseBlock + 1) : nkb;
-    int count = 0;
+    static_assert(T::BR == kSparseBlock, "one mask row block per workgroup");
+    const int qb = q0 / kSparseBlock;
+    const uint8_t* row = BM + (size_t)bh * bm_stride + (size_t)qb * nkb;
+    const int kb_lim = CAUSAL ? min(nkb, qb + 1) : nkb;
     for (int base = 0; base < kb_lim; base += 64 * T::NW) {
       const int kb = base + tid;
-      const bool in = kb < kb_lim;
-      const bool f0 = in && row0[kb] != 0;
-      const bool f1 = in && has1 && row1[kb] != 0;
-      const uint64_t bal = __ballot(f0 || f1);
+      const bool keep = kb < kb_lim && row[kb] != 0;
+      const uint64_t bal = __ballot(keep);
       const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
       if (lane == 0) wtot[w] = __popcll(bal);
       __syncthreads();
-      int off = count, tot = 0;
+      int off = nlist, tot = 0;
       for (int ww = 0; ww < T::NW; ++ww) {
         if (ww < w) off += wtot[ww];
         tot += wtot[ww];
       }
-      if (f0 || f1) tlist[off + below] = (uint16_t)(kb | (int(f0) << 14) | (int(f1) << 15));
-      count += tot;
+      if (keep) tlist[off + below] = (uint16_t)kb;
+      nlist += tot;
       __syncthreads();
     }
-    nkt = count * TPB;
+    nkt = nlist * TPB;
+    win0 = lane < nlist ? tlist[lane] : 0u;
+    win1 = 64 + lane < nlist ? tlist[64 + lane] : 0u;
   }
-  // Key tile of loop position j, and whether this wave's rows see its block.
+  // Key tile of loop position j (the window must hold entry j / TPB).
   auto tile_at = [&](int j) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE)
-      return (__builtin_amdgcn_readfirstlane(tlist[j / TPB]) & 0x3fff) * TPB + j % TPB;
-    else
+    if constexpr (SPARSE) {
+      // Pick the window register per lane first (one select, no branch),
+      // then read the entry's lane.
+      const int e = j / TPB - wbase;
+      const unsigned src = e < 64 ? win0 : win1;
+      const int kb = __builtin_amdgcn_readlane((int)src, e & 63);
+      return kb * TPB + j % TPB;
+    } else {
       return j;
+    }
   };
-  auto own_sees = [&](int j) __attribute__((always_inline)) -> bool {
-    if constexpr (SPARSE)
-      return (__builtin_amdgcn_readfirstlane(tlist[j / TPB]) >> (14 + wq)) & 1;
-    else
-      return true;
+  // Slide the window by 64 entries when position jmax would leave it.
+  auto window_for = [&](int jmax) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (jmax / TPB - wbase >= 128) {
+        wbase += 64;
+        win0 = win1;
+        const int e = wbase + 64 + lane;
+        win1 = e < nlist ? tlist[e] : 0u;
+      }
+    }
   };
 
   // ---- tile fetch: each wave moves LOADS KiB of the K (or V) tile ----------
@@ -370,11 +384,9 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
     // and V[j-2], whose last readers ran in iteration j-1 (closed by its
     // barrier), with K[j+4] and V[j+2], from inside the product sequence.
 
-    // Mask tile j where it crosses the causal diagonal or the end of the keys
-    // (block-sparse: or where this wave's row block does not see its block).
+    // Mask tile j where it crosses the causal diagonal or the end of the keys.
     const int key0 = tile_at(j) * T::BC;
-    const bool sees = own_sees(j);
-    if ((key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > qw0) || !sees) {
+    if ((key0 + T::BC > Lk) || (CAUSAL && key0 + T::BC - 1 > qw0)) {
       // Register r of key block kb2 holds key key0 + 4h + (kb2*32 + 8(r/4) + r%4);
       // it is visible iff that constant offset is <= lim.  The sign of
       // (lim - offset) selects -inf without compares.
@@ -382,7 +394,7 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
         constexpr int rb = decltype(RBc)::value;
         const int qrow = qw0 + 32 * rb + n;
         const int last = CAUSAL ? min(Lk - 1, qrow) : Lk - 1;
-        const int lim = sees ? last - key0 - 4 * h : -(1 << 30);
+        const int lim = last - key0 - 4 * h;
         static_for<0, 16 * T::NKB>([&](auto Ec) __attribute__((always_inline)) {
           constexpr int e = decltype(Ec)::value, kb2 = e >> 4, r = e & 15;
           constexpr int off = kb2 * 32 + 8 * (r >> 2) + (r & 3);
@@ -567,6 +579,7 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
   // Four iterations per trip (j = 1..4 mod 4) as one straight-line chain, so
   // ring slots and register roles are compile-time in every body.
   for (int j = 1; j < nkt; j += 4) {
+    window_for(min(j + 7, nkt - 1));  // this trip fetches up to tile j + 7
     iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA);
     if (j + 1 >= nkt) break;
     iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB);
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(64 * FwdTile<D>::NW, 1) void fwd_bf16_kernel(
 
 template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, SPARSE>;
   const int n_qt = (a.Lq + T::BR - 1) / T::BR;
   const dim3 grid((unsigned)(n_qt * a.BH));
   // c = |scale| log2(e), kept > 0 so masked (-inf) scores give exactly 0; a
@@ -655,7 +668,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  static_assert(FwdTile<128>::BR == kFwdBf16RowsPerBlock, "tile table out of sync");
+  static_assert(FwdTile<128, false>::BR == kFwdBf16RowsPerBlock, "tile table out of sync");
   if (a.block_mask) return a.d == 64 ? launch_d<64, true>(a, stream) : launch_d<128, true>(a, stream);
   return a.d == 64 ? launch_d<64, false>(a, stream) : launch_d<128, false>(a, stream);
 }
