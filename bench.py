@@ -20,7 +20,10 @@ oracle is timed on a bounded sample of the same workload.
 
 After the timed steps, the key-split forward (fa_fwd_splitkv) is measured on
 the decode workload (B8 H32, one query row, 16384 keys, d128) and reported
-under "decode" with its HBM roofline; it is not part of "value".
+under "decode" with its HBM roofline, and the block-sparse forward
+(fa_fwd_blocksparse, same shape as the main step, causal, sliding window of
+four 128-key blocks plus the first block) under "blocksparse"; neither is
+part of "value".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
@@ -201,6 +204,61 @@ def bench_decode(steps, warmup, with_cpu):
     return out
 
 
+def bench_blocksparse(steps, warmup, with_cpu):
+    """Block-sparse forward on the benchmark shape (B1 H32 L4096 d128,
+    causal) with a sliding window of 4 blocks plus the first block."""
+    from workloads import window_block_mask
+    w = WORKLOADS[BENCH_WORKLOAD]
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16", seed=w.seed,
+                                              amp=w.amp))
+    nb = -(-w.Lq // fa.SPARSE_BLOCK)
+    bm_cpu = window_block_mask(nb)
+    bm = bm_cpu.to(dev)
+    O = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+    rows = torch.arange(w.Lq) // fa.SPARSE_BLOCK
+    vis = bm_cpu.bool()[rows[:, None], rows[None, :]] & torch.ones(w.Lq, w.Lk, dtype=torch.bool).tril()
+    pairs = int(vis.sum()) * w.B * w.H
+    flops_alg = 4.0 * w.d * pairs
+    call = lambda: fa.fa_fwd_blocksparse(q, k, v, bm, scale=w.scale, causal=True, out=O, lse=lse)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    achieved = flops_alg / (ms * 1e-3) / 1e12
+    out = {
+        "workload": f"block-sparse forward B{w.B} H{w.H} L{w.Lq} d{w.d} causal, 128x128 blocks: "
+                    "window of 4 blocks + first block",
+        "visible_pairs": pairs, "dense_causal_pairs": w.B * w.H * w.Lq * (w.Lq + 1) // 2,
+        "us": round(ms * 1e3, 2),
+        "roofline": {"kernel": "fwd_bf16_kernel (block-sparse)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "algorithmic_flops": flops_alg, "traffic": None},
+        "cpu_baseline": None,
+    }
+    if with_cpu:
+        import oracle
+        from workloads import to_f64
+        qh, kh, vh = (to_f64(t[:, :1]) for t in make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16",
+                                                             seed=w.seed, amp=w.amp))
+        t0 = time.perf_counter()
+        oracle.attn_fwd_blocksparse(qh, kh, vh, w.scale, True, bm_cpu.numpy(),
+                                    block=fa.SPARSE_BLOCK)
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(flops_alg / w.H / el / 1e12, 5), "unit": "TFLOP/s",
+                               "kind": "oracle",
+                               "sample": f"1 of {w.H} heads (fp64 numpy, full masked S), {el:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,7 +266,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
-                    help="skip the key-split (decode) forward measured after the main step")
+                    help="skip the decode and block-sparse forwards measured after the main step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -328,6 +386,8 @@ def main():
     if not args.no_decode:
         # Measured after the timed steps above; not part of value.
         line["decode"] = bench_decode(args.steps, max(args.warmup, 20), not args.no_cpu_baseline)
+        line["blocksparse"] = bench_blocksparse(args.steps, max(args.warmup, 20),
+                                                not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

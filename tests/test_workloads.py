@@ -41,3 +41,12 @@ def test_workload_table():
     w = WORKLOADS["fwd_f32_B1H1L128d64"]
     q, k, v = workload_inputs(w)
     assert q.dtype == torch.float32 and q.shape == (1, 1, 128, 64)
+
+
+def test_window_block_mask():
+    from workloads import window_block_mask
+    m = window_block_mask(6, window=2)
+    assert m.dtype == torch.uint8 and m.shape == (6, 6)
+    assert m.tolist() == [[1, 0, 0, 0, 0, 0], [1, 1, 0, 0, 0, 0], [1, 1, 1, 0, 0, 0],
+                          [1, 0, 1, 1, 0, 0], [1, 0, 0, 1, 1, 0], [1, 0, 0, 0, 1, 1]]
+    assert window_block_mask(3, window=1, first=False).tolist() == [[1, 0, 0], [0, 1, 0], [0, 0, 1]]

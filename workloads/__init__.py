@@ -124,6 +124,18 @@ def sample_rows(H, L, n, seed, B=1):
     return rows
 
 
+def window_block_mask(n_blocks, window=4, first=True):
+    """Block mask [n_blocks, n_blocks] (uint8 CPU tensor): row block i keeps
+    key blocks i-window+1 .. i (a sliding window) and, with ``first``, key
+    block 0 -- a local window plus the leading tokens.  An input of the
+    block-sparse forward; no attention arithmetic."""
+    i = torch.arange(n_blocks)
+    keep = (i[:, None] - i[None, :] < window) & (i[None, :] <= i[:, None])
+    if first:
+        keep |= (i[None, :] == 0)
+    return keep.to(torch.uint8)
+
+
 def to_f64(x):
     """CPU float64 numpy copy of a tensor (any dtype, any device)."""
     return x.detach().to("cpu", torch.float64).numpy()
