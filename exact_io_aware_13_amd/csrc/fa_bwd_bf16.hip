@@ -10,7 +10,8 @@
 //
 // Three kernels, no atomics, every output written once by one workgroup in
 // a fixed summation order (so the backward is bitwise deterministic):
-//  1. pre:   D_i = rowsum(dO * O) and lse in base 2, per query row.
+//  1. pre:   -D_i = -rowsum(dO * O) and lse in base 2, per query row (the
+//            negated D starts the dK/dV kernel's dP accumulation).
 //  2. dK/dV: key-stationary.  One workgroup = 4 waves = 128 keys of one
 //            slice (32 per wave); K and V rows stay in registers as
 //            matrix-product operands, dK and dV accumulate in registers
@@ -64,7 +65,7 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. D statistic and base-2 lse
+// 1. D statistic (stored negated) and base-2 lse
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && c == 0) {
-    Dvec[row] = acc;
+    Dvec[row] = -acc;
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -309,7 +310,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     u32x4 afr[T::NALL];
     f32x16 s[2], dp[2];
     unsigned pp[2][8], pd[2][8];
-    f32x4 lr[2][4], er[2][4];
+    f32x4 lr[2][4];
+    // -D of the tile's rows as the dP chains' initial accumulator: the
+    // products then leave dP - D in place.
+    f32x16 nd[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 e = *reinterpret_cast<const f32x4*>(eb_ + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nd[qb][4 * g + i] = e[i];
+      }
     float xs[2][4][4], ps[2][4][4];
     // Causal: element (qb, g, i) of this lane is visible iff
     // q0 + 32 qb + 8 g + 4 h + i >= key.
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       if constexpr (o.kind == OP_S) {
         s[o.qb] = mma(as_bf16x8(afr[i]), kf[o.ks], o.ks == 0 ? z : s[o.qb]);
       } else if constexpr (o.kind == OP_DP) {
-        dp[o.qb] = mma(as_bf16x8(afr[i]), vf[o.ks], o.ks == 0 ? z : dp[o.qb]);
+        dp[o.qb] = mma(as_bf16x8(afr[i]), vf[o.ks], o.ks == 0 ? nd[o.qb] : dp[o.qb]);
       } else if constexpr (o.kind == OP_DV) {
         u32x4 b;
         b.x = pp[o.qb][o.hf * 4 + 0];
@@ -373,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       } else {
         float d4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d4[i] = ps[qb][g][i] * (dp[qb][4 * g + i] - er[qb][g][i]);
+        for (int i = 0; i < 4; ++i) d4[i] = ps[qb][g][i] * dp[qb][4 * g + i];
         pp[qb][2 * g] = pack_bf16x2(ps[qb][g][0], ps[qb][g][1]);
         pp[qb][2 * g + 1] = pack_bf16x2(ps[qb][g][2], ps[qb][g][3]);
         pd[qb][2 * g] = pack_bf16x2(d4[0], d4[1]);
@@ -401,9 +413,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         constexpr int l0 = spread(3 * g, 12, T::GC, T::NA) - 2, e0 = spread(3 * g + 2, 12, T::GC, T::NA) - 2;
         constexpr int l1 = spread(3 * g, 12, T::GD, T::ND) - 2, e1 = spread(3 * g + 2, 12, T::GD, T::ND) - 2;
         if constexpr (l0 == sl) lr[0][g] = *reinterpret_cast<const f32x4*>(lb_ + 8 * g + 4 * h);
-        if constexpr (e0 == sl) er[0][g] = *reinterpret_cast<const f32x4*>(eb_ + 8 * g + 4 * h);
         if constexpr (l1 == sl) lr[1][g] = *reinterpret_cast<const f32x4*>(lb_ + 32 + 8 * g + 4 * h);
-        if constexpr (e1 == sl) er[1][g] = *reinterpret_cast<const f32x4*>(eb_ + 32 + 8 * g + 4 * h);
       });
       static_for<0, 12>([&](auto Uc) __attribute__((always_inline)) {
         constexpr int uu = decltype(Uc)::value;
@@ -728,7 +738,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
       constexpr int e = decltype(Ec)::value, rb = e % T::RB, x = e / T::RB, kb = x / 4, g = x % 4;
       float d4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d4[i] = pv[rb][kb][4 * g + i] * (dpv[rb][kb][4 * g + i] - dd[rb]);
+      for (int i = 0; i < 4; ++i) d4[i] = pv[rb][kb][4 * g + i] * (dpv[rb][kb][4 * g + i] + dd[rb]);
       ds_cur[rb][kb][2 * g] = pack_bf16x2(d4[0], d4[1]);
       ds_cur[rb][kb][2 * g + 1] = pack_bf16x2(d4[2], d4[3]);
       pin(ds_cur[rb][kb][2 * g]);

@@ -38,7 +38,7 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;   // [BH, Lq] row statistic (workspace)
+  float* Dvec;   // [BH, Lq] row statistic (workspace; bf16 path: -D, fp32 path: D)
   float* lse2;   // [BH, Lq] lse * log2(e) (workspace)
   int BH, Lq, Lk, d;
   float scale;

@@ -130,6 +130,7 @@ FA_API fa_status fa_fwd_blocksparse(fa_dtype in_dtype, fa_dtype out_dtype,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: the D statistic
+ * (bf16 path: stored negated)
  * and lse in base 2 ([B,H,Lq] float each, each padded to a multiple of 256
  * bytes).  Linear in Lq; independent of the number of scores.  Returns 0
  * for sizes fa_bwd would reject.
