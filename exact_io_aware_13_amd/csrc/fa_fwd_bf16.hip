@@ -111,7 +111,7 @@ struct FwdTile {
 };
 
 template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__((64 * FwdTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) void fwd_bf16_kernel(
+__global__ __launch_bounds__((64 * FwdTile<D, SPARSE>::NW), ((SPARSE && D == 128) ? 2 : 1)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign,
