@@ -1,9 +1,11 @@
 // Exact attention forward, bf16 inputs, fp32 accumulation, gfx950.
 //
-// One workgroup = 256 query rows of one (batch, head) slice: at d=128 8
-// waves of one 32-row block each (two waves per SIMD), at d=64 4 waves of two
-// blocks.  The Q rows stay in registers for the whole key loop; K and V
-// stream through LDS in tiles of 32 (d=128) or 64 (d=64) keys, and an
+// One workgroup = 256 query rows of one (batch, head) slice, 8 waves of one
+// 32-row block each (two waves per SIMD); launches that would give fewer
+// than two such workgroups per compute unit use 128-row workgroups of 4
+// waves instead (two per compute unit).  The Q rows stay in registers for
+// the whole key loop; K and V stream through LDS in tiles of 32 (d=128) or
+// 64 (d=64) keys, and an
 // online softmax keeps a running max m, a running sum l and an unnormalised
 // output per row, rescaling both by exp(m_old - m_new) when the max moves
 // ("How Flash Attention Improves Transformer Memory Efficiency ...",
@@ -71,15 +73,16 @@
 namespace fa {
 namespace {
 
-template <int D, bool SPARSE>
+template <int D, bool HALF>
 struct FwdTile {
-  // d=128: 8 waves of one 32-row block, two waves per SIMD (each fits in
-  // 256 registers), so one wave's softmax runs while the other's matrix
-  // products do; d=64: 4 waves of two blocks.  Block-sparse: half the waves,
-  // so that a workgroup's 128 rows are exactly one row block of the mask
-  // (two workgroups share a compute unit).
-  static constexpr int NW = (D == 128 ? 8 : 4) / (SPARSE ? 2 : 1);  // waves per workgroup
-  static constexpr int RB = D == 128 ? 1 : 2;     // 32-row blocks per wave
+  // 256 rows: 8 waves of one 32-row block, two waves per SIMD (each fits
+  // in 256 registers), so one wave's softmax runs while the other's matrix
+  // products do.  HALF: 128 rows, 4 waves, two workgroups per compute unit
+  // -- for launches that would otherwise give fewer than two workgroups per
+  // compute unit, and for the block-sparse forward (one mask row block per
+  // workgroup).
+  static constexpr int NW = HALF ? 4 : 8;  // waves per workgroup
+  static constexpr int RB = 1;             // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   // Keys per tile: at d=128 a 32-key tile keeps the softmax working set
   // (two score sets, two probability sets) inside the 256 VGPRs the vector
@@ -110,13 +113,16 @@ struct FwdTile {
   static constexpr int prog_begin(int p) { return (p * NPROG + NPHYS - 1) / NPHYS; }
 };
 
-template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
-__global__ __launch_bounds__((64 * FwdTile<D, SPARSE>::NW), ((SPARSE && D == 128) ? 2 : 1)) void fwd_bf16_kernel(
+// MODE: 0 dense, 256 rows per workgroup; 1 dense, 128 rows; 2 block-sparse,
+// 128 rows.
+template <int D, bool CAUSAL, bool OUT_F32, int MODE>
+__global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
-  using T = FwdTile<D, SPARSE>;
+  using T = FwdTile<D, MODE != 0>;
+  constexpr bool SPARSE = MODE == 2;
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
@@ -641,9 +647,9 @@ __global__ __launch_bounds__((64 * FwdTile<D, SPARSE>::NW), ((SPARSE && D == 128
   }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32, bool SPARSE>
+template <int D, bool CAUSAL, bool OUT_F32, int MODE>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  using T = FwdTile<D, SPARSE>;
+  using T = FwdTile<D, MODE != 0>;
   const int n_qt = (a.Lq + T::BR - 1) / T::BR;
   const dim3 grid((unsigned)(n_qt * a.BH));
   // c = |scale| log2(e), kept > 0 so masked (-inf) scores give exactly 0; a
@@ -651,26 +657,31 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   float c = fabsf(a.scale) * kLog2e;
   if (c < 1e-30f) c = 1e-30f;
   const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, SPARSE>), grid, dim3(64 * T::NW), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MODE>), grid, dim3(64 * T::NW), 0,
                      stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                      static_cast<const uint16_t*>(a.V), a.O, a.lse, a.BH, a.Lq, a.Lk, n_qt, c,
                      qsign, a.block_mask, a.bm_stride, a.nqb, a.nkb);
   return hipGetLastError();
 }
 
-template <int D, bool SPARSE>
+template <int D, int MODE>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
   if (a.causal)
-    return a.out_f32 ? launch<D, true, true, SPARSE>(a, stream) : launch<D, true, false, SPARSE>(a, stream);
-  return a.out_f32 ? launch<D, false, true, SPARSE>(a, stream) : launch<D, false, false, SPARSE>(a, stream);
+    return a.out_f32 ? launch<D, true, true, MODE>(a, stream) : launch<D, true, false, MODE>(a, stream);
+  return a.out_f32 ? launch<D, false, true, MODE>(a, stream) : launch<D, false, false, MODE>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   static_assert(FwdTile<128, false>::BR == kFwdBf16RowsPerBlock, "tile table out of sync");
-  if (a.block_mask) return a.d == 64 ? launch_d<64, true>(a, stream) : launch_d<128, true>(a, stream);
-  return a.d == 64 ? launch_d<64, false>(a, stream) : launch_d<128, false>(a, stream);
+  if (a.block_mask) return a.d == 64 ? launch_d<64, 2>(a, stream) : launch_d<128, 2>(a, stream);
+  // 256-row workgroups unless that gives fewer than two per compute unit
+  // (gfx950: 256 compute units); then 128-row ones, which also halve the
+  // longest workgroup's work under a causal mask.
+  const int64_t wgs256 = (int64_t)((a.Lq + 255) / 256) * a.BH;
+  if (wgs256 < 512) return a.d == 64 ? launch_d<64, 1>(a, stream) : launch_d<128, 1>(a, stream);
+  return a.d == 64 ? launch_d<64, 0>(a, stream) : launch_d<128, 0>(a, stream);
 }
 
 }  // namespace fa
