@@ -17,8 +17,8 @@
 //            matrix-product operands, dK and dV accumulate in registers
 //            over every 64-row query tile that can see the keys.
 //  3. dQ:    query-stationary, laid out like the forward.  One workgroup =
-//            256 query rows (d=128: 8 waves x 32 rows, d=64: 4 waves x 64);
-//            K and V stream through LDS, and per key tile the wave
+//            256 query rows, 8 waves x 32 rows; K and V stream through
+//            LDS, and per key tile the wave
 //            recomputes S^T and dP^T, forms dS^T, and accumulates
 //            dQ^T = K^T dS^T in registers.
 // Splitting dQ off costs two extra matrix products per (key, query) tile
@@ -472,10 +472,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTile {
-  // d=128: 8 waves of one 32-row block (two waves per SIMD, each within 256
-  // registers); d=64: 4 waves of two blocks.
-  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
-  static constexpr int RB = D == 128 ? 1 : 2;     // 32-row blocks per wave
+  // 8 waves of one 32-row block (two waves per SIMD, each within 256
+  // registers).
+  static constexpr int NW = 8;                    // waves per workgroup
+  static constexpr int RB = 1;                    // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   static constexpr int BC = D == 128 ? 32 : 64;   // keys per tile
   static constexpr int NKB = BC / 32;             // 32-key blocks per tile

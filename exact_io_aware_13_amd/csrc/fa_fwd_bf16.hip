@@ -5,9 +5,9 @@
 // than two such workgroups per compute unit use 128-row workgroups of 4
 // waves instead (two per compute unit).  The Q rows stay in registers for
 // the whole key loop; K and V stream through LDS in tiles of 32 (d=128) or
-// 64 (d=64) keys, and an
-// online softmax keeps a running max m, a running sum l and an unnormalised
-// output per row, rescaling both by exp(m_old - m_new) when the max moves
+// 64 (d=64) keys, and an online softmax keeps a running max m, a running
+// sum l and an unnormalised output per row, rescaling both by
+// exp(m_old - m_new) when the max moves
 // ("How Flash Attention Improves Transformer Memory Efficiency ...",
 // sections "Block-Wise Processing Algorithm" and "The Three Running
 // Statistics"; "What Is FlashAttention?", section "What FlashAttention does
