@@ -39,7 +39,7 @@ from .attention import (
     attn_bwd_heads,
 )
 from .splitkv import attn_fwd_keyrange, merge_partials
-from .blocksparse import attn_fwd_blocksparse, block_visible
+from .blocksparse import attn_bwd_blocksparse, attn_fwd_blocksparse, block_visible
 
 __all__ = [
     "visible_mask",
@@ -50,5 +50,6 @@ __all__ = [
     "attn_fwd_keyrange",
     "merge_partials",
     "attn_fwd_blocksparse",
+    "attn_bwd_blocksparse",
     "block_visible",
 ]

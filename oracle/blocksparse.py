@@ -63,3 +63,39 @@ def attn_fwd_blocksparse(q, k, v, scale, causal, block_mask, block=128):
             O[b, h][seen] = np.exp(S - lse_r[:, None]) @ v[b, h]
             lse[b, h][seen] = lse_r
     return O, lse
+
+
+def attn_bwd_blocksparse(q, k, v, dO, scale, causal, block_mask, block=128):
+    """Gradients of <dO, O> for block-sparse attention.
+
+    The chain rule through the definition above (the same formulas as the
+    dense backward, with P zero outside the kept pairs): D_i = sum_c dO_ic
+    O_ic, dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dQ = scale dS K,
+    dK = scale dS^T Q.  A row that sees no key has P = 0 and contributes
+    nothing.  Returns (dq, dk, dv) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, H, Lq, _ = q.shape
+    Lk = k.shape[2]
+    bm = np.asarray(block_mask)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            vis = block_visible(bm if bm.ndim == 2 else bm[b, h], Lq, Lk, block, causal)
+            seen = vis.any(axis=1)
+            S = np.where(vis, scale * (q[b, h] @ k[b, h].T), -np.inf)
+            P = np.zeros((Lq, Lk))
+            m = S[seen].max(axis=1, keepdims=True)
+            lse = m[:, 0] + np.log(np.exp(S[seen] - m).sum(axis=1))
+            P[seen] = np.exp(S[seen] - lse[:, None])
+            O = P @ v[b, h]
+            D = (dO[b, h] * O).sum(axis=1)
+            dv[b, h] = P.T @ dO[b, h]
+            dP = dO[b, h] @ v[b, h].T
+            dS = P * (dP - D[:, None])
+            dq[b, h] = scale * (dS @ k[b, h])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+    return dq, dk, dv

@@ -452,8 +452,62 @@ def pin_blocksparse_loops(oracle):
     assert np.isneginf(lse[0, 1, 0]), "row 0 of head 1 sees no key (block 0,0 dropped)"
 
 
+def pin_blocksparse_bwd_all_kept(oracle):
+    # Keeping every block gives the dense gradients.
+    q, k, v = _qkv(54, 1, 2, 9, 11, 3)
+    dO = _rng(55).standard_normal((1, 2, 9, 3))
+    bm = np.ones((3, 3), dtype=np.uint8)
+    for causal in (False, True):
+        ref = oracle.attn_bwd(q, k, v, dO, 0.7, causal)
+        got = oracle.attn_bwd_blocksparse(q, k, v, dO, 0.7, causal, bm, block=4)
+        for a, r, n in zip(got, ref, "qkv"):
+            _close(a, r, 1e-13, f"all kept: d{n} equals dense")
+
+
+def pin_blocksparse_bwd_block_diagonal(oracle):
+    # Block-diagonal mask: each block's gradients are the dense backward of
+    # that block alone; no gradient crosses blocks.
+    q, k, v = _qkv(56, 1, 1, 10, 10, 2)
+    dO = _rng(57).standard_normal((1, 1, 10, 2))
+    got = oracle.attn_bwd_blocksparse(q, k, v, dO, 0.9, True, np.eye(3, dtype=np.uint8), block=4)
+    for a in range(0, 10, 4):
+        b = min(a + 4, 10)
+        ref = oracle.attn_bwd(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], dO[:, :, a:b], 0.9, True)
+        for x, r, n in zip(got, ref, "qkv"):
+            _close(x[:, :, a:b], r, 1e-13, f"diagonal block {a}: d{n}")
+
+
+def pin_blocksparse_bwd_finite_differences(oracle):
+    # Central differences of <dO, O> on a tiny case (block 2, causal, a row
+    # that sees nothing): the analytic gradients match to 1e-7.
+    r = _rng(58)
+    q, k, v = (r.standard_normal((1, 1, n, 2)) for n in (5, 6, 6))
+    dO = r.standard_normal((1, 1, 5, 2))
+    bm = np.array([[0, 1, 1], [1, 0, 1], [1, 1, 0]], dtype=np.uint8)
+    s, eps = 0.8, 1e-6
+
+    def loss(q_, k_, v_):
+        O, _ = oracle.attn_fwd_blocksparse(q_, k_, v_, s, True, bm, block=2)
+        return float((O * dO).sum())
+
+    dq, dk, dv = oracle.attn_bwd_blocksparse(q, k, v, dO, s, True, bm, block=2)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            args_m = [xm if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        _close(g, num, 1e-7, f"finite differences d{name}")
+    assert np.all(dq[0, 0, 0] == 0), "row 0 sees no key: its dQ is 0"
+
+
 BLOCKSPARSE_PINS = [pin_blocksparse_all_kept, pin_blocksparse_block_diagonal,
-                    pin_blocksparse_key_column, pin_blocksparse_loops]
+                    pin_blocksparse_key_column, pin_blocksparse_loops,
+                    pin_blocksparse_bwd_all_kept, pin_blocksparse_bwd_block_diagonal,
+                    pin_blocksparse_bwd_finite_differences]
 
 SPLITKV_PINS = [pin_keyrange_whole, pin_keyrange_single_key, pin_keyrange_causal_rows,
                 pin_merge_partition, pin_merge_library]

@@ -104,6 +104,22 @@ def _transposed_visible(block_mask, Lq, Lk, block, causal):
     return bm[r[None, :], c[:, None]] & A.visible_mask(Lq, Lk, causal)
 
 
+def _bs_bwd_variant(change):
+    """A copy of the block-sparse backward with one term altered."""
+    real = BS.attn_bwd_blocksparse
+
+    def bwd(q, k, v, dO, scale, causal, block_mask, block=128):
+        dq, dk, dv = real(q, k, v, dO, scale, causal, block_mask, block)
+        return change(dq, dk, dv, np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(dO))
+    return bwd
+
+
+BLOCKSPARSE_BWD_MUTANTS = {
+    "dQ sign flipped": lambda dq, dk, dv, q, k, v, dO: (-dq, dk, dv),
+    "dK scaled twice": lambda dq, dk, dv, q, k, v, dO: (dq, 1.3 * dk, dv),
+}
+
+
 BLOCKSPARSE_MUTANTS = {
     "block mask read transposed": ("block_visible", _transposed_visible),
     "block index off by one row": ("block_visible", _vis_variant(lambda i, j, b: ((i + 1) // b, j // b))),
@@ -177,6 +193,25 @@ def test_splitkv_mutant_is_caught(name, monkeypatch):
 def test_blocksparse_mutant_is_caught(name, monkeypatch):
     attr, fn = BLOCKSPARSE_MUTANTS[name]
     monkeypatch.setattr(BS, attr, fn)
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.BLOCKSPARSE_PINS)
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+def test_blocksparse_bwd_ignoring_the_mask_is_caught(monkeypatch):
+    dense = lambda q, k, v, dO, scale, causal, block_mask, block=128: oracle.attn_bwd(
+        q, k, v, dO, scale, causal)
+    monkeypatch.setattr(BS, "attn_bwd_blocksparse", dense)
+    monkeypatch.setattr(oracle, "attn_bwd_blocksparse", dense)
+    with np.errstate(all="ignore"):
+        failed = _failures(oracle_pins.BLOCKSPARSE_PINS)
+    assert failed, "no pin caught the backward ignoring the block mask"
+
+
+@pytest.mark.parametrize("name", sorted(BLOCKSPARSE_BWD_MUTANTS))
+def test_blocksparse_bwd_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(BS, "attn_bwd_blocksparse", _bs_bwd_variant(BLOCKSPARSE_BWD_MUTANTS[name]))
+    monkeypatch.setattr(oracle, "attn_bwd_blocksparse", BS.attn_bwd_blocksparse)
     with np.errstate(all="ignore"):
         failed = _failures(oracle_pins.BLOCKSPARSE_PINS)
     assert failed, f"no pin caught the planted mistake: {name}"
