@@ -9,6 +9,7 @@ exposes the same calls on torch tensors:
                                                  128x128 blocks removed
     fa_bwd(q, k, v, o, do, lse, scale, causal) -> (dQ, dK, dV)
     fa_bwd_prepare / fa_bwd_dkdv / fa_bwd_dq     (the backward's stages)
+    fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, ...) -> (dQ, dK, dV)
     fa_bwd_workspace_bytes(dtype, B, H, Lq, Lk, d)
     fa_fwd_splitkv(q, k, v, scale, causal, nsplit)  -> (O, lse), keys split
                                                        in ranges (decode shape)
@@ -16,14 +17,16 @@ exposes the same calls on torch tensors:
     attention(q, k, v, causal=False, scale=None)   (autograd)
 """
 
-from .binding import (FlashAttentionFn, attention, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
+from .binding import (FlashAttentionFn, attention, fa_bwd, fa_bwd_blocksparse, fa_bwd_dkdv,
+                      fa_bwd_dq,
                       fa_bwd_prepare, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_blocksparse,
                       fa_fwd_splitkv, SPARSE_BLOCK,
                       fa_fwd_splitkv_default_splits, fa_fwd_splitkv_merge,
                       fa_fwd_splitkv_partial, fa_fwd_splitkv_workspace_bytes)
 from ._lib import FaError, LIB_PATH, load as load_library
 
-__all__ = ["attention", "fa_fwd", "fa_fwd_blocksparse", "SPARSE_BLOCK", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+__all__ = ["attention", "fa_fwd", "fa_fwd_blocksparse", "SPARSE_BLOCK", "fa_bwd",
+           "fa_bwd_blocksparse", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_default_splits", "FlashAttentionFn",

@@ -21,7 +21,7 @@ STATUS_NAMES = {
     4: "FA_ERR_ALIGN", 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG",
 }
 
-EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
+EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_default_splits", "fa_status_str", "fa_version")
@@ -48,6 +48,9 @@ def _declare(lib):
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
                            vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_blocksparse.restype = i32
+    lib.fa_bwd_blocksparse.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
+                                       vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_prepare.restype = i32
     lib.fa_bwd_prepare.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_dkdv.restype = i32

@@ -167,6 +167,48 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
     return dq, dk, dv
 
 
+def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=False, dq=None,
+                       dk=None, dv=None, workspace=None):
+    """dQ, dK, dV through libfa's ``fa_bwd_blocksparse``: the backward of
+    :func:`fa_fwd_blocksparse` with the same ``block_mask``."""
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
+                         ("o", o, (B, H, Lq, d)), ("do", do, (B, H, Lq, d))):
+        _check_tensor(name, t, dev, q.dtype, shp)
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    nqb, nkb = -(-Lq // SPARSE_BLOCK), -(-Lk // SPARSE_BLOCK)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    if tuple(block_mask.shape) == (nqb, nkb):
+        slices = 1
+    elif tuple(block_mask.shape) == (B, H, nqb, nkb):
+        slices = B * H
+    else:
+        raise ValueError(f"block_mask must be [{nqb}, {nkb}] or [{B}, {H}, {nqb}, {nkb}]")
+    _check_tensor("block_mask", block_mask, dev, torch.uint8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, dev, q.dtype, ref.shape)
+    need = fa_bwd_workspace_bytes(q.dtype, B, H, Lq, Lk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_bwd_blocksparse(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(o), _ptr(do), _ptr(lse), float(scale),
+                                        int(bool(causal)), _ptr(block_mask), slices, _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                        _stream(dev))
+    _lib.check(st)
+    return dq, dk, dv
+
+
 def _bwd_shapes(q, k, v, do):
     B, H, Lq, d = q.shape
     Lk = k.shape[2]

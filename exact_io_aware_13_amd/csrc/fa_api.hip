@@ -146,7 +146,8 @@ fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, i
                      int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
                      const void* O, const void* dO, const float* lse, float scale, int causal,
                      void* dQ, void* dK, void* dV, const void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, const uint8_t* block_mask = nullptr,
+                     int64_t mask_slices = 0) {
   if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
   if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
   const bool has_q = B * H * Lq > 0, has_k = B * H * Lk > 0;
@@ -185,6 +186,12 @@ fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, i
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal != 0;
+  if (block_mask) {
+    a.block_mask = block_mask;
+    a.nqb = (int)cdiv(Lq, fa::kSparseBlock);
+    a.nkb = (int)cdiv(Lk, fa::kSparseBlock);
+    a.bm_stride = mask_slices == 1 ? 0 : a.nqb * a.nkb;
+  }
   // Second line of defence: every pointer a launched kernel dereferences is
   // set (the checks above are per argument; this is per kernel).
   if (has_q && pre && !(a.O && a.dO && a.lse && a.Dvec && a.lse2)) return FA_ERR_NULL;
@@ -346,6 +353,27 @@ fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype, int64_t B, int64_t H, int64_t
   // The merge does not look at keys; one key keeps the shape checks valid.
   return splitkv_run(fa::kSplitKvMerge, FA_BF16, out_dtype, B, H, Lq, 1, d, nullptr, nullptr,
                      nullptr, 1.f, 0, nsplit, O, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+fa_status fa_bwd_blocksparse(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                             int64_t d, const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* lse, float scale, int causal,
+                             const uint8_t* block_mask, int64_t mask_slices, void* dQ, void* dK,
+                             void* dV, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (mask_slices != 1 && mask_slices != B * H) return FA_ERR_ARG;
+  const int64_t nqb = cdiv(Lq, fa::kSparseBlock), nkb = cdiv(Lk, fa::kSparseBlock);
+  if (nkb > fa::kSparseMaxKeyBlocks || nqb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
+  if (B * H * (Lq + Lk) > 0 && !block_mask) return FA_ERR_NULL;
+  return bwd_stages(fa::kBwdAll, in_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale, causal, dQ,
+                    dK, dV, workspace, workspace_bytes, stream, block_mask, mask_slices);
 }
 
 }  // extern "C"

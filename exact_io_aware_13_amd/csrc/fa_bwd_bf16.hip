@@ -147,13 +147,17 @@ constexpr KvOp kv_op(int i) {
   return o;
 }
 
-template <int D, bool CAUSAL>
+// SPARSE: block-sparse backward -- the workgroup's 128 keys are one key
+// block of the mask, and it visits only the 128-row query blocks whose mask
+// entry for that key block is set (a compacted list, read through register
+// windows as in the forward).
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int Lq, int Lk, float c,
-    float scale) {
+    float scale, const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = KvTile<D>;
   // Double-buffered query-side tiles, one LDS array per buffer, so the
   // compiler waits only for the loads a read depends on.
@@ -199,7 +203,61 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int n_qt = (Lq + T::BQ - 1) / T::BQ;
   const int qt0 = CAUSAL ? min(k0 / T::BQ, n_qt) : 0;
-  const int nsteps = n_qt - qt0;
+  int nsteps = n_qt - qt0;
+
+  // ---- block-sparse: the query blocks that see this key block --------------
+  constexpr int QPB = kSparseBlock / T::BQ;  // query tiles per mask block
+  __shared__ uint16_t qlist[SPARSE ? kSparseMaxKeyBlocks : 1];
+  __shared__ int wtot[SPARSE ? T::NW : 1];
+  int nlist = 0, wbase = 0;
+  unsigned win0 = 0, win1 = 0;
+  if constexpr (SPARSE) {
+    static_assert(T::BK == kSparseBlock, "one mask key block per workgroup");
+    const int kb = k0 / kSparseBlock;
+    const uint8_t* col = BM + (size_t)bh * bm_stride + kb;
+    const int qb_lo = CAUSAL ? kb : 0;
+    for (int base = qb_lo; base < nqb; base += 64 * T::NW) {
+      const int qb = base + tid;
+      const bool keep = qb < nqb && col[(size_t)qb * nkb] != 0;
+      const uint64_t bal = __ballot(keep);
+      const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
+      if (lane == 0) wtot[w] = __popcll(bal);
+      __syncthreads();
+      int off = nlist, tot = 0;
+      for (int ww = 0; ww < T::NW; ++ww) {
+        if (ww < w) off += wtot[ww];
+        tot += wtot[ww];
+      }
+      if (keep) qlist[off + below] = (uint16_t)qb;
+      nlist += tot;
+      __syncthreads();
+    }
+    nsteps = nlist * QPB;
+    win0 = lane < nlist ? qlist[lane] : 0u;
+    win1 = 64 + lane < nlist ? qlist[64 + lane] : 0u;
+  }
+  // Query tile of step t (past the last step: the first tile past the
+  // queries, which reads as zeros).
+  auto qtile = [&](int t) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) {
+      if (t >= nsteps) return n_qt;
+      const int e = t / QPB - wbase;
+      const unsigned src = e < 64 ? win0 : win1;
+      return __builtin_amdgcn_readlane((int)src, e & 63) * QPB + t % QPB;
+    } else {
+      return qt0 + t;
+    }
+  };
+  auto window_for = [&](int tmax) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (min(tmax, nsteps - 1) / QPB - wbase >= 128) {
+        wbase += 64;
+        win0 = win1;
+        const int e = wbase + 64 + lane;
+        win1 = e < nlist ? qlist[e] : 0u;
+      }
+    }
+  };
   // At least two tiles run when any is visible: a tile past the end of the
   // queries reads as zeros and adds exactly nothing, and one code path for
   // every workgroup keeps the accumulators in registers.
@@ -222,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // share one LDS base and differ in the immediate offset.
   auto fetch_unit = [&](auto Bc, int t, auto Uc) __attribute__((always_inline)) {
     constexpr int u = decltype(Uc)::value;
-    const int q0 = (qt0 + t) * T::BQ;
+    const int q0 = qtile(t) * T::BQ;
     if constexpr (u < T::QLOADS) {
       constexpr int i = u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -325,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     float xs[2][4][4], ps[2][4][4];
     // Causal: element (qb, g, i) of this lane is visible iff
     // q0 + 32 qb + 8 g + 4 h + i >= key.
-    const int lim = (qt0 + t) * T::BQ + 4 * h - key;
+    const int lim = qtile(t) * T::BQ + 4 * h - key;
 
     auto read_frag = [&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
@@ -443,9 +501,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // accumulator registers and copy them every tile), then an odd last one.
     int t = 2;
     for (; t + 1 < nrun; t += 2) {
+      window_for(t + 2);  // this pair fetches up to step t + 2
       step(IC<0>{}, std::false_type{}, t);
       step(IC<1>{}, std::false_type{}, t + 1);
     }
+    window_for(t + 1);
     if (t < nrun) step(IC<0>{}, std::false_type{}, t);
   }
 
@@ -496,12 +556,17 @@ struct DqTile {
   static_assert(LOADS >= 1, "tile split");
 };
 
-template <int D, bool CAUSAL>
+// SPARSE: block-sparse backward -- the workgroup's 256 rows are two row
+// blocks of the mask; it visits the key blocks either of them sees (a
+// compacted list with one flag per row block), and a wave whose row block
+// does not see a listed block zeroes that tile's probabilities.
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
-    int BH, int Lq, int Lk, int n_qt, float c, float scale) {
+    int BH, int Lq, int Lk, int n_qt, float c, float scale,
+    const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = DqTile<D>;
   // 4-slot rings for K and V, one LDS array per slot.
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
@@ -553,6 +618,68 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   int nkt = (Lk + T::BC - 1) / T::BC;
   if (CAUSAL) nkt = min(nkt, (q0 + T::BR - 1) / T::BC + 1);
 
+  // ---- block-sparse: key blocks either row block sees ------------------------
+  // Entry: key block in bits 0..13, bit 14 + b set if row block b sees it.
+  constexpr int TPB = kSparseBlock / T::BC;  // key tiles per mask block
+  __shared__ uint16_t klist[SPARSE ? kSparseMaxKeyBlocks : 1];
+  __shared__ int wtot[SPARSE ? T::NW : 1];
+  const int wq = (32 * T::RB * w) / kSparseBlock;  // this wave's row block
+  int nlist = 0, wbase = 0;
+  unsigned win0 = 0, win1 = 0;
+  if constexpr (SPARSE) {
+    static_assert(T::BR == 2 * kSparseBlock, "two mask row blocks per workgroup");
+    const int qb0 = q0 / kSparseBlock;
+    const bool has1 = qb0 + 1 < nqb;
+    const uint8_t* row0 = BM + (size_t)bh * bm_stride + (size_t)qb0 * nkb;
+    const uint8_t* row1 = row0 + nkb;
+    const int kb_lim = CAUSAL ? min(nkb, (q0 + T::BR - 1) / kSparseBlock + 1) : nkb;
+    for (int base = 0; base < kb_lim; base += 64 * T::NW) {
+      const int kb = base + tid;
+      const bool in = kb < kb_lim;
+      const bool f0 = in && row0[kb] != 0;
+      const bool f1 = in && has1 && row1[kb] != 0;
+      const uint64_t bal = __ballot(f0 || f1);
+      const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
+      if (lane == 0) wtot[w] = __popcll(bal);
+      __syncthreads();
+      int off = nlist, tot = 0;
+      for (int ww = 0; ww < T::NW; ++ww) {
+        if (ww < w) off += wtot[ww];
+        tot += wtot[ww];
+      }
+      if (f0 || f1) klist[off + below] = (uint16_t)(kb | (int(f0) << 14) | (int(f1) << 15));
+      nlist += tot;
+      __syncthreads();
+    }
+    nkt = nlist * TPB;
+    win0 = lane < nlist ? klist[lane] : 0u;
+    win1 = 64 + lane < nlist ? klist[64 + lane] : 0u;
+  }
+  auto entry_at = [&](int j) __attribute__((always_inline)) -> unsigned {
+    const int e = j / TPB - wbase;
+    const unsigned src = e < 64 ? win0 : win1;
+    return (unsigned)__builtin_amdgcn_readlane((int)src, e & 63);
+  };
+  // Key tile of loop position j, and whether this wave's row block sees it.
+  auto tile_at = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return (int)(entry_at(j) & 0x3fffu) * TPB + j % TPB;
+    else return j;
+  };
+  auto own_sees = [&](int j) __attribute__((always_inline)) -> bool {
+    if constexpr (SPARSE) return (entry_at(j) >> (14 + wq)) & 1u;
+    else return true;
+  };
+  auto window_for = [&](int jmax) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (min(jmax, nkt - 1) / TPB - wbase >= 128) {
+        wbase += 64;
+        win0 = win1;
+        const int e = wbase + 64 + lane;
+        win1 = e < nlist ? klist[e] : 0u;
+      }
+    }
+  };
+
   // ---- K / V tile fetch into ring slots -----------------------------------------
   int fetch_off[T::LOADS];
 #pragma unroll
@@ -565,7 +692,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     // Tiles past the last one re-fetch the last tile into a free slot, which
     // keeps the number of loads in flight the same every iteration.
     // One LDS base per tensor; load i adds i KiB through the immediate offset.
-    const int t = min(tile, nkt - 1);
+    const int t = tile_at(min(tile, nkt - 1));
     lds_void* kd = (lds_void*)(kslot(SLc) + w * T::LOADS * 1024);
     lds_void* vd = (lds_void*)(vslot(SLc) + w * T::LOADS * 1024);
     static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
@@ -764,12 +891,14 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, N1>(run);
 
-    // Causal: zero P^T where the key is past the row (key > query).
-    const int key0 = j * T::BC;
-    if (CAUSAL && key0 + T::BC - 1 > qw0) {
+    // Causal: zero P^T where the key is past the row (key > query);
+    // block-sparse: the whole tile when this wave's row block does not see it.
+    const int key0 = tile_at(j) * T::BC;
+    const bool sees = own_sees(j);
+    if ((CAUSAL && key0 + T::BC - 1 > qw0) || !sees) {
       static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
         constexpr int rb = decltype(RBc)::value;
-        const int lim = qw0 + 32 * rb + n - key0 - 4 * h;
+        const int lim = sees ? qw0 + 32 * rb + n - key0 - 4 * h : -(1 << 30);
         static_for<0, 16 * T::NKB>([&](auto Ec) __attribute__((always_inline)) {
           constexpr int e = decltype(Ec)::value, kb = e >> 4, r = e & 15;
           constexpr int off = kb * 32 + 8 * (r >> 2) + (r & 3);
@@ -791,6 +920,8 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     block_barrier();
   };
 
+  // A block-sparse workgroup whose rows see no key writes dQ = 0.
+  if (!SPARSE || nkt > 0) {
   // ---- prologue: dO rows and tile 0 landed, tile 1 in flight -------------------
   fetch(0, IC<0>{});
   __builtin_amdgcn_sched_barrier(0);  // tile 0's loads are issued first
@@ -805,11 +936,13 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   // up to three more.
   int j = 1;
   for (; j + 3 < nkt; j += 4) {
+    window_for(j + 5);  // this round fetches up to tile j + 5
     iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
     iter(IC<2>{}, std::false_type{}, j + 1, dskB, dskA);
     iter(IC<3>{}, std::false_type{}, j + 2, dskA, dskB);
     iter(IC<0>{}, std::false_type{}, j + 3, dskB, dskA);
   }
+  window_for(j + 4);
   if (j < nkt) {
     iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
     if (j + 1 < nkt) {
@@ -833,6 +966,8 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     case 2: last_dq(K2, dskA); break;
     default: last_dq(K3, dskB); break;
   }
+  }  // !SPARSE || nkt > 0
+  wait_vm<0>();  // the dO rows' loads, when no tile ran
 
   // ---- dQ = scale * accumulator, one query row per lane --------------------------
   const auto rdq = make_rsrc(dQ + qoff, (uint32_t)Lq * D * 2);
@@ -851,7 +986,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   using TK = KvTile<D>;
   using TQ = DqTile<D>;
@@ -862,14 +997,16 @@ void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
   const int n_kt = (a.Lk + TK::BK - 1) / TK::BK;
   if ((stages & kBwdDkDv) && n_kt > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)), dim3(64 * TK::NW),
-                       0, stream, Q, K, V, dO, a.lse2, a.Dvec, static_cast<uint16_t*>(a.dK),
-                       static_cast<uint16_t*>(a.dV), a.BH, a.Lq, a.Lk, c, a.scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)(n_kt * a.BH)),
+                       dim3(64 * TK::NW), 0, stream, Q, K, V, dO, a.lse2, a.Dvec,
+                       static_cast<uint16_t*>(a.dK), static_cast<uint16_t*>(a.dV), a.BH, a.Lq, a.Lk,
+                       c, a.scale, a.block_mask, a.bm_stride, a.nqb, a.nkb);
   const int n_qt = (a.Lq + TQ::BR - 1) / TQ::BR;
   if ((stages & kBwdDq) && n_qt > 0 && a.Lk > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(64 * TQ::NW),
-                       0, stream, Q, K, V, dO, a.lse2, a.Dvec, static_cast<uint16_t*>(a.dQ), a.BH,
-                       a.Lq, a.Lk, n_qt, c, a.scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)(n_qt * a.BH)),
+                       dim3(64 * TQ::NW), 0, stream, Q, K, V, dO, a.lse2, a.Dvec,
+                       static_cast<uint16_t*>(a.dQ), a.BH, a.Lq, a.Lk, n_qt, c, a.scale,
+                       a.block_mask, a.bm_stride, a.nqb, a.nkb);
 }
 
 template <int D>
@@ -881,8 +1018,13 @@ hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
                        0, stream, static_cast<const uint16_t*>(a.O),
                        static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
   }
-  if (a.causal) launch_main<D, true>(a, stages, stream);
-  else launch_main<D, false>(a, stages, stream);
+  if (a.block_mask) {
+    if (a.causal) launch_main<D, true, true>(a, stages, stream);
+    else launch_main<D, false, true>(a, stages, stream);
+  } else {
+    if (a.causal) launch_main<D, true, false>(a, stages, stream);
+    else launch_main<D, false, false>(a, stages, stream);
+  }
   return hipGetLastError();
 }
 

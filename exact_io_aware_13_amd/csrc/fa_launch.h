@@ -43,6 +43,9 @@ struct BwdArgs {
   int BH, Lq, Lk, d;
   float scale;
   bool causal;
+  // Block-sparse backward (bf16 only), as in FwdArgs; NULL for the dense one.
+  const uint8_t* block_mask = nullptr;
+  int bm_stride = 0, nqb = 0, nkb = 0;
 };
 
 // Backward stages, run in this order by the launchers for the stages set in

@@ -282,6 +282,28 @@ FA_API fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype,
                  const void* workspace, size_t workspace_bytes,
                  void* O, float* lse, hipStream_t stream);
 
+/*
+ * Block-sparse backward: fa_bwd for the attention fa_fwd_blocksparse
+ * computes, with the same block_mask and mask_slices.  The gradients are the
+ * chain rule through the masked definition (P is zero outside the kept
+ * pairs; a row that sees no key contributes nothing).  lse and O must be
+ * fa_fwd_blocksparse's outputs (rows that see no key: O = 0, lse = -inf).
+ * Workspace, layouts and status codes as for fa_bwd; supported: in_dtype
+ * FA_BF16, d in {64, 128}, ceil(Lq/128) and ceil(Lk/128) <= 4096 (else
+ * FA_ERR_UNSUPPORTED).  The key-side kernel visits only the query blocks
+ * that see its key block; the query side visits the key blocks either of a
+ * workgroup's two 128-row blocks sees.
+ */
+FA_API fa_status fa_bwd_blocksparse(fa_dtype in_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse,
+                 float scale, int causal,
+                 const uint8_t* block_mask, int64_t mask_slices,
+                 void* dQ, void* dK, void* dV,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 FA_API const char* fa_status_str(fa_status s);
 

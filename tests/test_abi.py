@@ -247,3 +247,15 @@ def test_blocksparse_rejects(lib, kw, status):
 def test_blocksparse_accepts_per_slice_mask_count(lib):
     assert _bs(lib, B=2, H=3, slices=6, Lq=0) == OK
     assert _bs(lib, B=2, H=3, slices=5, Lq=0) == ARG
+
+
+def test_bwd_blocksparse_rejects(lib):
+    ws = lib.fa_bwd_workspace_bytes(BF16, 1, 2, 300, 300, 128)
+    call = lambda **kw: lib.fa_bwd_blocksparse(
+        kw.get("dt", BF16), 1, 2, 300, kw.get("Lk", 300), 128, P, P, P, P, P, P, 0.1, 1,
+        kw.get("mask", P + 1), kw.get("slices", 1), P, P, P, P, kw.get("ws", ws), None)
+    assert call(dt=F32) == UNSUP
+    assert call(slices=3) == ARG
+    assert call(mask=None) == NULL
+    assert call(ws=8) == WS
+    assert call(Lk=4096 * 128 + 1) == UNSUP

@@ -129,3 +129,57 @@ def test_invalid_calls_are_rejected():
     assert e.value.name == "FA_ERR_UNSUPPORTED"
     with pytest.raises(ValueError):
         fa.fa_fwd_blocksparse(q, k, v, torch.ones((3, 2), dtype=torch.uint8, device=device()))
+
+
+# ---- block-sparse backward --------------------------------------------------
+
+from tests.gpu_util import BF16_GRAD_REL, rel_to_max  # noqa: E402
+
+BWD_CASES = [
+    # B, H, L, d, causal, per_slice, density
+    (1, 2, 256, 128, False, False, 0.5),
+    (1, 2, 384, 128, True, True, 0.6),
+    (2, 2, 500, 64, True, False, 0.5),
+    (1, 3, 640, 64, False, True, 0.4),
+    (1, 2, 1000, 128, True, True, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}H{}L{}d{}-c{}-s{}-p{}".format(*c))
+def test_blocksparse_backward_matches_oracle(case):
+    B, H, L, d, causal, per_slice, density = case
+    q, k, v, do = make_inputs(B, H, L, L, d, "bf16", seed=L + d, with_dO=True)
+    nb = -(-L // BLK)
+    bm = random_mask((B, H, nb, nb) if per_slice else (nb, nb), density, seed=3 * L + 1)
+    if per_slice:
+        bm[0, 0, 0, :] = 0  # first row block of slice (0, 0) sees no key
+    else:
+        bm[0, :] = 0
+    scale = 1.0 / math.sqrt(d)
+    ref = oracle.attn_bwd_blocksparse(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, causal,
+                                      bm.numpy(), block=BLK)
+    qd, kd, vd, dod, bmd = to_dev(q, k, v, do, bm)
+    announce(f"blocksparse bwd {case}")
+    O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=scale, causal=causal)
+    grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
+        err = rel_to_max(to_f64(g), r)
+        assert err <= BF16_GRAD_REL, f"{case} {name}: rel-to-max {err:.3e}"
+    # Rows that see no key get exactly zero dQ.
+    assert torch.all(grads[0][0, 0, :BLK] == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_all_blocks_kept_equals_dense_bitwise(d, causal):
+    B, H, L = 1, 2, 768
+    q, k, v, do = to_dev(*make_inputs(B, H, L, L, d, "bf16", seed=31, with_dO=True))
+    bm = torch.ones((L // BLK, L // BLK), dtype=torch.uint8, device=device())
+    announce(f"blocksparse bwd all kept d{d} causal {causal}")
+    O, lse = fa.fa_fwd(q, k, v, causal=causal)
+    dense = fa.fa_bwd(q, k, v, O, do, lse, causal=causal)
+    sparse = fa.fa_bwd_blocksparse(q, k, v, O, do, lse, bm, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(dense, sparse):
+        assert torch.equal(a, b)
