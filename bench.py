@@ -21,9 +21,9 @@ oracle is timed on a bounded sample of the same workload.
 After the timed steps, the key-split forward (fa_fwd_splitkv) is measured on
 the decode workload (B8 H32, one query row, 16384 keys, d128) and reported
 under "decode" with its HBM roofline, and the block-sparse forward
-(fa_fwd_blocksparse, same shape as the main step, causal, sliding window of
-four 128-key blocks plus the first block) under "blocksparse"; neither is
-part of "value".
+and its backward (fa_fwd_blocksparse / fa_bwd_blocksparse, same shape as the
+main step, causal, sliding window of four 128-key blocks plus the first
+block) under "blocksparse"; neither is part of "value".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
@@ -221,23 +221,36 @@ def bench_blocksparse(steps, warmup, with_cpu):
     vis = bm_cpu.bool()[rows[:, None], rows[None, :]] & torch.ones(w.Lq, w.Lk, dtype=torch.bool).tril()
     pairs = int(vis.sum()) * w.B * w.H
     flops_alg = 4.0 * w.d * pairs
-    call = lambda: fa.fa_fwd_blocksparse(q, k, v, bm, scale=w.scale, causal=True, out=O, lse=lse)
+    do = make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16", seed=w.seed, amp=w.amp,
+                     with_dO=True)[3].to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(torch.bfloat16, w.B, w.H, w.Lq, w.Lk, w.d),
+                     dtype=torch.uint8, device=dev)
+    fwd = lambda: fa.fa_fwd_blocksparse(q, k, v, bm, scale=w.scale, causal=True, out=O, lse=lse)
+    bwd = lambda: fa.fa_bwd_blocksparse(q, k, v, O, do, lse, bm, scale=w.scale, causal=True,
+                                        dq=dq, dk=dk, dv=dv, workspace=ws)
     for _ in range(warmup):
-        call()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        call()
-    e1.record()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fwd()
+        ev[i][1].record()
+        bwd()
+        ev[i][2].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_b = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     achieved = flops_alg / (ms * 1e-3) / 1e12
     out = {
         "workload": f"block-sparse forward B{w.B} H{w.H} L{w.Lq} d{w.d} causal, 128x128 blocks: "
                     "window of 4 blocks + first block",
         "visible_pairs": pairs, "dense_causal_pairs": w.B * w.H * w.Lq * (w.Lq + 1) // 2,
         "us": round(ms * 1e3, 2),
+        "bwd_us": round(ms_b * 1e3, 2),
+        "bwd_tflops_visible_pairs": round(2.5 * flops_alg / (ms_b * 1e-3) / 1e12, 2),
         "roofline": {"kernel": "fwd_bf16_kernel (block-sparse)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
