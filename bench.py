@@ -397,10 +397,13 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_decode:
-        # Measured after the timed steps above; not part of value.
-        line["decode"] = bench_decode(args.steps, max(args.warmup, 20), not args.no_cpu_baseline)
-        line["blocksparse"] = bench_blocksparse(args.steps, max(args.warmup, 20),
-                                                not args.no_cpu_baseline)
+        # Measured after the timed steps above; not part of value.  A failure
+        # here is recorded in the line instead of losing the main measurement.
+        for key, fn in (("decode", bench_decode), ("blocksparse", bench_blocksparse)):
+            try:
+                line[key] = fn(args.steps, max(args.warmup, 20), not args.no_cpu_baseline)
+            except Exception as e:  # noqa: BLE001
+                line[key] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
