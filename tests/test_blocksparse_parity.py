@@ -183,3 +183,25 @@ def test_backward_all_blocks_kept_equals_dense_bitwise(d, causal):
     torch.cuda.synchronize()
     for a, b in zip(dense, sparse):
         assert torch.equal(a, b)
+
+
+def test_backward_window_pattern_benchmark_size_two_heads():
+    # The launch the benchmark times: B1 H32 L4096 d128 causal, window of 4
+    # blocks + the first block; two full heads against the oracle.
+    from workloads import window_block_mask
+    w = WORKLOADS[BENCH_WORKLOAD]
+    q, k, v, do = make_inputs(w.B, w.H, w.Lq, w.Lk, w.d, "bf16", seed=w.seed, amp=w.amp,
+                              with_dO=True)
+    bm = window_block_mask(w.Lq // BLK)
+    qd, kd, vd, dod, bmd = to_dev(q, k, v, do, bm)
+    announce("blocksparse bwd window pattern B1 H32 L4096 d128 causal")
+    O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=w.scale, causal=True)
+    grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 17):
+        sl = lambda t: to_f64(t[:, h:h + 1])
+        ref = oracle.attn_bwd_blocksparse(sl(q), sl(k), sl(v), sl(do), w.scale, True, bm.numpy(),
+                                          block=BLK)
+        for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
+            err = rel_to_max(to_f64(g[:, h:h + 1]), r)
+            assert err <= BF16_GRAD_REL, f"head {h} {name}: rel-to-max {err:.3e}"
