@@ -88,3 +88,22 @@ def test_backward_at_the_largest_key_length_invariants():
     s_dv = (dv64.sum(0) - want).abs().max().item()
     assert s_dv <= 1e-3 * dv64.abs().sum(0).max().item() + 1e-2, f"sum of dV rows off by {s_dv}"
     assert torch.isfinite(dq).all()
+
+
+def test_largest_query_length_causal():
+    # Query and output offsets at the edge: Lq at the largest accepted length
+    # against 100 keys, causal (rows from 99 on see every key).  Sampled rows
+    # against the oracle; the backward through its two invariants.
+    Lk = 100
+    q, k, v, do = make_inputs(1, 1, LK_MAX, Lk, D, "bf16", seed=44, with_dO=True)
+    qd, kd, vd, dod = (t.to(device()) for t in (q, k, v, do))
+    announce(f"forward and backward at Lq = {LK_MAX}, Lk = {Lk}, causal")
+    O, lse = fa.fa_fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, O, dod, lse, causal=True)
+    torch.cuda.synchronize()
+    _check_rows(O, lse, q, k, v, [0, 50, 99, 12345, LK_MAX - 1], causal=True)
+    dk64, dv64 = dk[0, 0].double(), dv[0, 0].double()
+    assert dk64.sum(0).abs().max().item() <= 1e-3 * dk64.abs().sum(0).max().item()
+    want = do[0, 0].double().sum(0).to(dv64.device)
+    assert (dv64.sum(0) - want).abs().max().item() <= 1e-3 * dv64.abs().sum(0).max().item() + 1e-2
+    assert torch.isfinite(dq).all()
