@@ -205,3 +205,50 @@ def test_backward_window_pattern_benchmark_size_two_heads():
         for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
             err = rel_to_max(to_f64(g[:, h:h + 1]), r)
             assert err <= BF16_GRAD_REL, f"head {h} {name}: rel-to-max {err:.3e}"
+
+
+# ---- lists longer than one register window (128 entries) ---------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_key_block_list_forward_and_backward(d):
+    # 40000 keys = 313 key blocks at density 0.7: the key-block lists of the
+    # forward and of the dQ kernel run past two windows of 128 entries.
+    B, H, Lq, Lk = 1, 1, 256, 40000
+    q, k, v, do = make_inputs(B, H, Lq, Lk, d, "bf16", seed=51, with_dO=True)
+    bm = random_mask((-(-Lq // BLK), -(-Lk // BLK)), 0.7, seed=52)
+    assert int(bm[0].sum()) > 128 and int(bm[1].sum()) > 128
+    scale = 1.0 / math.sqrt(d)
+    O_ref, lse_ref = oracle.attn_fwd_blocksparse(to_f64(q), to_f64(k), to_f64(v), scale, False,
+                                                 bm.numpy(), block=BLK)
+    ref = oracle.attn_bwd_blocksparse(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, False,
+                                      bm.numpy(), block=BLK)
+    qd, kd, vd, dod, bmd = to_dev(q, k, v, do, bm)
+    announce(f"blocksparse long key list d{d}")
+    O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=scale)
+    grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=scale)
+    torch.cuda.synchronize()
+    _check(O, lse, O_ref, lse_ref, f"long key list d{d}")
+    for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
+        err = rel_to_max(to_f64(g), r)
+        assert err <= BF16_GRAD_REL, f"long key list d{d} {name}: rel-to-max {err:.3e}"
+
+
+def test_long_query_block_list_backward():
+    # 40000 queries = 313 query blocks at density 0.7: the dK/dV kernel's
+    # query-block list runs past two windows of 128 entries.
+    B, H, Lq, Lk, d = 1, 1, 40000, 256, 128
+    q, k, v, do = make_inputs(B, H, Lq, Lk, d, "bf16", seed=53, with_dO=True)
+    bm = random_mask((-(-Lq // BLK), -(-Lk // BLK)), 0.7, seed=54)
+    bm[:, 0] = 1  # every row block sees at least one key block
+    assert int(bm[:, 0].sum()) > 128 and int(bm[:, 1].sum()) > 128
+    scale = 1.0 / math.sqrt(d)
+    ref = oracle.attn_bwd_blocksparse(to_f64(q), to_f64(k), to_f64(v), to_f64(do), scale, False,
+                                      bm.numpy(), block=BLK)
+    qd, kd, vd, dod, bmd = to_dev(q, k, v, do, bm)
+    announce("blocksparse long query list")
+    O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=scale)
+    grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=scale)
+    torch.cuda.synchronize()
+    for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
+        err = rel_to_max(to_f64(g), r)
+        assert err <= BF16_GRAD_REL, f"long query list {name}: rel-to-max {err:.3e}"
