@@ -468,8 +468,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // Row statistics of group g, two slots before the unit that needs them.
       static_for<0, 4>([&](auto Gc) __attribute__((always_inline)) {
         constexpr int g = decltype(Gc)::value;
-        constexpr int l0 = spread(3 * g, 12, T::GC, T::NA) - 2, e0 = spread(3 * g + 2, 12, T::GC, T::NA) - 2;
-        constexpr int l1 = spread(3 * g, 12, T::GD, T::ND) - 2, e1 = spread(3 * g + 2, 12, T::GD, T::ND) - 2;
+        constexpr int l0 = spread(3 * g, 12, T::GC, T::NA) - 2;
+        constexpr int l1 = spread(3 * g, 12, T::GD, T::ND) - 2;
         if constexpr (l0 == sl) lr[0][g] = *reinterpret_cast<const f32x4*>(lb_ + 8 * g + 4 * h);
         if constexpr (l1 == sl) lr[1][g] = *reinterpret_cast<const f32x4*>(lb_ + 32 + 8 * g + 4 * h);
       });
