@@ -26,7 +26,7 @@ ARCH = "gfx950"
 # scores are -inf, which both flags keep exact), and without them every
 # fmaxf input is first re-quieted by an extra max instruction.
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-munsafe-fp-atomics",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
