@@ -45,12 +45,17 @@
 //
 // Softmax arithmetic runs in base 2: p = exp2(s * c - m) with c =
 // |scale| * log2(e) folded into one FMA (a negative scale is applied by
-// negating Q, which is exact in bf16); the row max is taken on the raw dot
-// products.  The reference max m is moved only when a row's max exceeds it
-// by more than 2^8: any reference gives the same O = acc / l and lse = m +
-// log2 l exactly, and keeping it fixed skips most rescales of the output
-// accumulator (probabilities then stay <= 2^8, far from overflow).  l sums
-// the fp32 probabilities; the value product takes them rounded to bf16.
+// negating Q, which is exact in bf16).  Any reference m gives the same
+// O = acc / l and lse = m + log2 l exactly, so m is not a running max: a
+// tile's probabilities are formed against the current m, and only when a
+// lane's sum of them exceeds 2^12 (or m is still the initial -3e38, which
+// makes them infinite) does a uniform branch take the row max of the tile
+// (raw dot products, one cross-half exchange), move m to it, rescale l and
+// the output accumulator and form the tile's probabilities again.  In
+// practice that happens on a row's first tile and rarely after, which
+// takes the per-tile max reduction out of the vector work; probabilities
+// stay <= 2^12, far from overflow.  l sums the fp32 probabilities; the
+// value product takes them rounded to bf16.
 // Tiles that are fully masked for some rows (causal diagonal band) are still
 // multiplied; their probabilities are exactly 0.
 //
@@ -72,6 +77,14 @@
 
 namespace fa {
 namespace {
+
+// Softmax reference before a row has seen a key: finite (so a masked score,
+// -inf, still gives exp2(-inf - m) = 0 and never -inf - -inf), and far
+// below any score, so the first visible key makes the tile's sum infinite
+// and moves the reference.
+constexpr float kInitialRef = -3.0e38f;
+// A lane's probability sum over one tile above which the reference moves.
+constexpr float kRescaleSum = 4096.f;
 
 template <int D, bool HALF>
 struct FwdTile {
@@ -99,12 +112,10 @@ struct FwdTile {
   static_assert(LOADS <= 4, "immediate load offsets reach 3 KiB");
   static constexpr int NFRAG = NKB * KS;          // K fragments per tile (= V fragments)
   static_assert(NFRAG == (BC / 16) * DB, "one K and one V fragment per step");
-  // Softmax slot program (all row blocks): row-max chains, running
-  // statistics, 4-probability groups in three stages, running sums.
-  static constexpr int NMAXP = 2 * NKB;           // max chains per row block (8 scores each)
+  // Softmax slot program (all row blocks): 4-probability groups in three
+  // stages, then the tile's probability sums.
   static constexpr int NGROUP = RB * 4 * NKB;     // 4-probability groups per iteration
-  static constexpr int SL_STATS = RB * NMAXP;
-  static constexpr int SL_GROUPS = SL_STATS + RB;
+  static constexpr int SL_GROUPS = 0;
   static constexpr int SL_SUMS = SL_GROUPS + 3 * NGROUP;
   static constexpr int NPROG = SL_SUMS + RB;      // program slots
   static constexpr int NPHYS = 2 * RB * NFRAG;    // matrix-product slots per iteration
@@ -313,7 +324,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   float m[T::RB], l[T::RB];
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb) {
-    m[rb] = -INFINITY;
+    m[rb] = kInitialRef;
     l[rb] = 0.f;
   }
 
@@ -414,57 +425,27 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
       });
     }
 
-    float mxp[T::RB][T::NMAXP], rs[T::RB][4], alpha[T::RB], base[T::RB];
+    float rs[T::RB][4], tsum[T::RB];
     float xg[T::NGROUP][4];  // probability groups in flight between stages
 #pragma unroll
     for (int rb = 0; rb < T::RB; ++rb) {
-      alpha[rb] = 1.f;
-      base[rb] = 0.f;
+      tsum[rb] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[rb][i] = 0.f;
     }
-    // Vector-ALU work placed after matrix-product slot SL (4 slots per step).
-    // Slots [0, SL_STATS): one row-max chain over 8 scores each; then the
-    // running statistics of each row block; then groups of 4 probabilities,
-    // each moving through three stages on consecutive slots (FMA, exp2, pack
-    // and sum), so no instruction waits right behind its producer; then the
-    // running sums.
+    // Vector-ALU work placed after the matrix-product slots: groups of 4
+    // probabilities, each moving through three stages on consecutive slots
+    // (FMA, exp2, pack and sum), so no instruction waits right behind its
+    // producer; then the tile's sums.
     auto slot_work = [&](auto SLc) __attribute__((always_inline)) {
       constexpr int sl = decltype(SLc)::value;
-      if constexpr (sl < T::SL_STATS) {
-        constexpr int rb = sl % T::RB, k = sl / T::RB, kb2 = k >> 1, r0 = (k & 1) * 8;
-        const f32x16& x = s_cur[rb][kb2];
-        float mm = fmaxf(fmaxf(x[r0], x[r0 + 1]), x[r0 + 2]);
-        mm = fmaxf(fmaxf(mm, x[r0 + 3]), x[r0 + 4]);
-        mm = fmaxf(fmaxf(mm, x[r0 + 5]), x[r0 + 6]);
-        mxp[rb][k] = fmaxf(mm, x[r0 + 7]);
-        pin(mxp[rb][k]);
-      } else if constexpr (sl < T::SL_GROUPS) {
-        constexpr int rb = sl - T::SL_STATS;
-        float mx = mxp[rb][0];
-        static_for<1, T::NMAXP>([&](auto Kc) __attribute__((always_inline)) {
-          mx = fmaxf(mx, mxp[rb][decltype(Kc)::value]);
-        });
-        mx = halves_max(mx);
-        const float mt = mx * c;  // -inf stays -inf (c > 0)
-        const float m_new = (mt > m[rb] + 8.f) ? mt : m[rb];
-        // Dense: tile 0 holds key 0 for every row, so m_new is finite from
-        // the first tile on; exp2(0) = 1 exactly when the reference stays.
-        // Block-sparse: a row may have seen nothing yet (m_new = -inf); the
-        // reference is then 0, so p = exp2(-inf) = 0 and alpha = 0.
-        const float ref = (SPARSE && m_new == -INFINITY) ? 0.f : m_new;
-        alpha[rb] = fast_exp2(m[rb] - ref);
-        m[rb] = m_new;
-        base[rb] = ref;
-        pin(alpha[rb]);
-        pin(base[rb]);
-      } else if constexpr (sl < T::SL_SUMS) {
+      if constexpr (sl < T::SL_SUMS) {
         constexpr int t = sl - T::SL_GROUPS, g = t / 3, stage = t % 3;
         constexpr int rb = g % T::RB, eg = g / T::RB, kb2 = eg >> 2, r0 = (eg & 3) * 4;
         if constexpr (stage == 0) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            xg[g][e] = __builtin_fmaf(s_cur[rb][kb2][r0 + e], c, -base[rb]);
+            xg[g][e] = __builtin_fmaf(s_cur[rb][kb2][r0 + e], c, -m[rb]);
             pin(xg[g][e]);
           }
         } else if constexpr (stage == 1) {
@@ -483,8 +464,8 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
         }
       } else if constexpr (sl < T::SL_SUMS + T::RB) {
         constexpr int rb = sl - T::SL_SUMS;
-        l[rb] = alpha[rb] * l[rb] + ((rs[rb][0] + rs[rb][1]) + (rs[rb][2] + rs[rb][3]));
-        pin(l[rb]);
+        tsum[rb] = (rs[rb][0] + rs[rb][1]) + (rs[rb][2] + rs[rb][3]);
+        pin(tsum[rb]);
       }
     };
 
@@ -542,18 +523,51 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
         __builtin_amdgcn_sched_barrier(0);
       });
     });
-    // Rescale after P(j-1)V(j-1) is in, before P(j)V(j) is added.
-    bool moved = false;
+    // Tile j's probabilities grew past the bound on some lane (or a row's
+    // reference is still the initial one): move the reference to the row
+    // max, rescale l and the output accumulator (which holds tiles up to
+    // j-1 at this point) and form tile j's probabilities again.  Every lane
+    // of the wave takes the branch; for a row whose max does not exceed its
+    // reference nothing changes (alpha = 1, the same probabilities).
+    bool big = false;
 #pragma unroll
-    for (int rb = 0; rb < T::RB; ++rb) moved |= alpha[rb] != 1.f;
-    if (__any(moved)) {
+    for (int rb = 0; rb < T::RB; ++rb) big |= tsum[rb] > kRescaleSum;
+    if (__any(big)) {
 #pragma unroll
-      for (int rb = 0; rb < T::RB; ++rb)
+      for (int rb = 0; rb < T::RB; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < T::NKB; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[rb][kb2][r]);
+        // A row that sees no key of the tile keeps its reference (mx * c =
+        // -inf); the initial reference is finite, so no -inf - -inf arises.
+        const float m_new = fmaxf(m[rb], halves_max(mx) * c);
+        const float alpha = fast_exp2(m[rb] - m_new);
+        m[rb] = m_new;
+        l[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha[rb];
+          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < T::NKB; ++kb2)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[e] = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][4 * q4 + e], c, -m_new));
+            pk_cur[rb][kb2][2 * q4] = pack_bf16x2(x[0], x[1]);
+            pk_cur[rb][kb2][2 * q4 + 1] = pack_bf16x2(x[2], x[3]);
+            sum[q4] += (x[0] + x[1]) + (x[2] + x[3]);
+          }
+        tsum[rb] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
+      }
     }
+#pragma unroll
+    for (int rb = 0; rb < T::RB; ++rb) l[rb] += tsum[rb];
     wait_vm<4 * T::LOADS>();  // loads of iteration j-2 and older landed
     block_barrier();
   };

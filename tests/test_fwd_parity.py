@@ -162,3 +162,42 @@ def test_autograd_wrapper_forward_matches():
     torch.cuda.synchronize()
     assert torch.equal(O, O2)
     assert device().type == "cuda"
+
+
+# ---- softmax reference moves after the first tile ---------------------------
+# The forward keeps a row's softmax reference until a tile's probabilities
+# against it grow past a bound; these inputs make later tiles' scores exceed
+# the first tile's by far, so the reference moves (once, several times, or
+# by hundreds of units), with both masks and a ragged tail.
+
+def _reference_move_inputs(kind, Lq, Lk, d, seed):
+    q, k, v = make_inputs(1, 2, Lq, Lk, d, "bf16", seed=seed)
+    qf, kf = q.float(), k.float()
+    if kind == "ramp":        # scores grow along the keys: many moves
+        kf = kf * torch.linspace(0.5, 6.0, Lk).view(1, 1, Lk, 1)
+    elif kind == "late_key":  # one late key wins every row by ~30 log2 units
+        qf[..., 0] = 4.0
+        kf[:, :, Lk - 5] = 0.0
+        kf[:, :, Lk - 5, 0] = 60.0
+    elif kind == "spread":    # large score spread everywhere
+        qf, kf = qf * 3.0, kf * 3.0
+    # Peaked rows put most weight on a few keys, each probability rounded to
+    # bf16 for the value product; the output error of that rounding scales
+    # with |V|, so V is halved to stay inside the bf16 bound (the reference
+    # moves depend on Q and K only).
+    return qf.to(torch.bfloat16), kf.to(torch.bfloat16), (0.5 * v.float()).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["ramp", "late_key", "spread"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reference_moves_late(kind, causal, d):
+    Lq, Lk = 300, 1000
+    q, k, v = _reference_move_inputs(kind, Lq, Lk, d, seed=71 + d)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"fwd reference moves {kind} d{d} causal={causal}")
+    O, lse = fa.fa_fwd(*to_dev(q, k, v), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attn_fwd(f64(q), f64(k), f64(v), scale, causal)
+    assert np.isfinite(f64(O)).all() and np.isfinite(f64(lse)).all()
+    assert_bf16_fwd(fwd_errors(f64(O), f64(lse), O_ref, lse_ref), f"{kind} d{d} causal={causal}")
