@@ -759,6 +759,13 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     lse2[rb] = load4f(rl, (uint32_t)qrow * 4);
     dd[rb] = load4f(re, (uint32_t)qrow * 4);
   }
+  // -D of the lane's row in every element: the initial accumulator of each
+  // dP^T chain, so the products leave dP - D in place.
+  f32x16 ndv[T::RB];
+#pragma unroll
+  for (int rb = 0; rb < T::RB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndv[rb][r] = dd[rb];
   // dO rows [q0, q0 + BR) into GR (same swizzled layout as the K/V tiles).
 #pragma unroll
   for (int i = 0; i < T::GLOADS; ++i) {
@@ -851,7 +858,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
         s[rb][kb] = mma(as_bf16x8(afr[i0]), qf[rb][ks], ks == 0 ? z : s[rb][kb]);
       } else if constexpr (i < N1) {
         constexpr int f = (i - T::NS) / T::RB, kb = f % T::NKB, ks = f / T::NKB;
-        dpv[rb][kb] = mma(as_bf16x8(afr[i0]), as_bf16x8(bfr[i - T::NS]), ks == 0 ? z : dpv[rb][kb]);
+        dpv[rb][kb] = mma(as_bf16x8(afr[i0]), as_bf16x8(bfr[i - T::NS]), ks == 0 ? ndv[rb] : dpv[rb][kb]);
       } else {
         dq_product(afr[i0], ds_prev, IC<(i - N1) / T::RB>{}, IC<rb>{});
       }
@@ -870,7 +877,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
       constexpr int e = decltype(Ec)::value, rb = e % T::RB, x = e / T::RB, kb = x / 4, g = x % 4;
       float d4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d4[i] = pv[rb][kb][4 * g + i] * (dpv[rb][kb][4 * g + i] + dd[rb]);
+      for (int i = 0; i < 4; ++i) d4[i] = pv[rb][kb][4 * g + i] * dpv[rb][kb][4 * g + i];
       ds_cur[rb][kb][2 * g] = pack_bf16x2(d4[0], d4[1]);
       ds_cur[rb][kb][2 * g + 1] = pack_bf16x2(d4[2], d4[3]);
       pin(ds_cur[rb][kb][2 * g]);
