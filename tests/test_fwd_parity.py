@@ -179,6 +179,10 @@ def _reference_move_inputs(kind, Lq, Lk, d, seed):
         qf[..., 0] = 4.0
         kf[:, :, Lk - 5] = 0.0
         kf[:, :, Lk - 5, 0] = 60.0
+    elif kind == "huge_gap":  # one late key wins every row by ~1000 log2 units
+        qf[..., 0] = 4.0
+        kf[:, :, Lk - 5] = 0.0
+        kf[:, :, Lk - 5, 0] = 2000.0
     elif kind == "spread":    # large score spread everywhere
         qf, kf = qf * 3.0, kf * 3.0
     # Peaked rows put most weight on a few keys, each probability rounded to
@@ -189,7 +193,7 @@ def _reference_move_inputs(kind, Lq, Lk, d, seed):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("kind", ["ramp", "late_key", "spread"])
+@pytest.mark.parametrize("kind", ["ramp", "late_key", "huge_gap", "spread"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_reference_moves_late(kind, causal, d):
     Lq, Lk = 300, 1000
