@@ -46,7 +46,8 @@
 // runs S^T and dP^T of key tile j and then dQ^T of tile j-1; P of tile j is
 // formed while the dP^T products run and dS of tile j while the dQ^T
 // products of tile j-1 run.  K and V tiles come into 4-slot LDS rings two
-// tiles ahead.
+// tiles ahead; the wave's Q and dO rows (B operands of S^T and dP^T) stay in
+// registers.
 //
 // Every 16-byte chunk c of a Q/dO/K/V row r sits at chunk c ^ swz(r) in LDS
 // (the forward's layout); all fragment reads are free of bank conflicts.
@@ -552,7 +553,6 @@ struct DqTile {
   // Products per iteration: S^T of tile j, dP^T of tile j, dQ^T of tile j-1.
   static constexpr int NS = RB * NFRAG, NP = RB * NFRAG, NQ = RB * NT;
   static constexpr int NDS = RB * NKB * 4;        // 4-element groups per tile
-  static constexpr int GLOADS = BR * ROWB / 1024 / NW;  // dO rows: load instructions per wave
   static_assert(LOADS >= 1, "tile split");
 };
 
@@ -577,15 +577,6 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char V1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V2[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char V3[T::TILEB];
-  // The workgroup's dO rows stay in LDS for the whole kernel: B operands of
-  // dP^T.  (Q's rows stay in registers; both would not fit next to the dQ
-  // accumulators.)  Its lower alignment makes the compiler place it after
-  // the ring slots: the ring reads, whose slot changes every tile, then sit
-  // below 64 KiB and take the slot base in the instruction's 16-bit offset
-  // instead of an address add per read (and ~50 fewer registers); the dO
-  // reads use loop-invariant addresses either way.  256 bytes keeps the
-  // rows aligned to the 64 banks.
-  __shared__ __attribute__((aligned(256))) char GR[T::BR * T::ROWB];
   auto kslot = [&](auto I) __attribute__((always_inline)) -> char* {
     constexpr int v = decltype(I)::value;
     if constexpr (v == 0) return K0;
@@ -747,15 +738,19 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     return a;
   };
 
-  // ---- per-row operands: Q rows (B operands of S^T), lse2 and D -------------
+  // ---- per-row operands: Q and dO rows (B operands of S^T and dP^T), lse2
+  // and D; all stay in registers for the whole kernel -----------------------
   bf16x8 qf[T::RB][T::KS];
+  u32x4 gf[T::RB][T::KS];
   float lse2[T::RB], dd[T::RB];
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb) {
     const int qrow = qw0 + 32 * rb + n;
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
+    for (int ks = 0; ks < T::KS; ++ks) {
       qf[rb][ks] = as_bf16x8(load16(rq, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2));
+      gf[rb][ks] = load16(rdo, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2);
+    }
     lse2[rb] = load4f(rl, (uint32_t)qrow * 4);
     dd[rb] = load4f(re, (uint32_t)qrow * 4);
   }
@@ -766,19 +761,6 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   for (int rb = 0; rb < T::RB; ++rb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndv[rb][r] = dd[rb];
-  // dO rows [q0, q0 + BR) into GR (same swizzled layout as the K/V tiles).
-#pragma unroll
-  for (int i = 0; i < T::GLOADS; ++i) {
-    const int row = (w * T::GLOADS + i) * T::RPK + lane / T::CPR;
-    const int chunk = (lane % T::CPR) ^ swz<D>(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (lds_void*)(GR + (w * T::GLOADS + i) * 1024), 16,
-                                             (uint32_t)((q0 + row) * D + chunk * 8) * 2, 0, 0, 0);
-  }
-  // dO fragment of row block rb, step ks (B operand of dP^T).
-  auto gread = [&](int rb, int ks) __attribute__((always_inline)) {
-    return lds_read16(GR, (32 * T::RB * w + 32 * rb) * T::ROWB + koffs[ks]);
-  };
-
   f32x16 dq[T::RB][T::DB];
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb)
@@ -834,13 +816,13 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     f32x16 s[T::RB][T::NKB], dpv[T::RB][T::NKB];
     float pv[T::RB][T::NKB][16];
     u32x4 afr[NALL], bfr[T::NP];
-    // One K / V / K^T fragment feeds both row blocks; dP^T also reads its
-    // dO fragment.
+    // One K / V / K^T fragment feeds both row blocks; dP^T also takes its
+    // dO fragment from registers.
     auto read_frag = [&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
       if constexpr (i >= T::NS && i < N1) {
         constexpr int x = i - T::NS, f = x / T::RB;
-        bfr[x] = gread(x % T::RB, f / T::NKB);
+        bfr[x] = gf[x % T::RB][f / T::NKB];
       }
       if constexpr (i % T::RB == 0) {
         if constexpr (i < T::NS) afr[i] = fread(kb_, i / T::RB);
@@ -934,7 +916,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
 
   // A block-sparse workgroup whose rows see no key writes dQ = 0.
   if (!SPARSE || nkt > 0) {
-  // ---- prologue: dO rows and tile 0 landed, tile 1 in flight -------------------
+  // ---- prologue: tile 0 landed, tile 1 in flight ---------------------------------
   fetch(0, IC<0>{});
   __builtin_amdgcn_sched_barrier(0);  // tile 0's loads are issued first
   fetch(1, IC<1>{});
@@ -979,7 +961,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     default: last_dq(K3, dskB); break;
   }
   }  // !SPARSE || nkt > 0
-  wait_vm<0>();  // the dO rows' loads, when no tile ran
+  wait_vm<0>();  // the loads of the tiles past the last one
 
   // ---- dQ = scale * accumulator, one query row per lane --------------------------
   const auto rdq = make_rsrc(dQ + qoff, (uint32_t)Lq * D * 2);
