@@ -25,6 +25,19 @@ and its backward (fa_fwd_blocksparse / fa_bwd_blocksparse, same shape as the
 main step, causal, sliding window of four 128-key blocks plus the first
 block) under "blocksparse"; neither is part of "value".
 
+Every other workload of the study is measured too, under "workloads": the
+fp32 forward at B1 H1 L128 d64, the bf16 forward at B4 H16 L1024 d64 without
+and with the causal mask, the forward and the backward at the headline shape,
+the long-context forward at B1 H8 L32768 d128 and the backward at B2 H16
+L2048 d128.  Each is captured R calls at a time in a HIP graph (so host-side
+launch cost does not enter the time of the small ones) and replayed 5 times;
+the median per-call time gives TFLOP/s, the fraction of the matrix-core (or,
+for fp32, vector) peak, and algorithmic HBM GB/s against 8 TB/s.  The fp64
+oracle is timed beside each on the host: all cores, and one core for the
+small shapes; the long-context oracle computes 256 sampled rows per head and
+says so.  The shader clock is measured with a spin kernel that counts clock
+cycles, alone and while the headline step runs.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
 
@@ -45,6 +58,7 @@ from workloads import BENCH_WORKLOAD, DECODE_WORKLOAD, WORKLOADS, make_inputs  #
 
 METRIC = "attn fwd+bwd TFLOP/s & % bf16 MFMA peak, B1 H32 L4096 d128 causal"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak (published)
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak (published)
 MIN_WARMUP_S = 0.25           # least busy time before the timed steps
 CSRC = os.path.join(ROOT, "exact_io_aware_13_amd", "csrc")
@@ -272,6 +286,233 @@ def bench_blocksparse(steps, warmup, with_cpu):
     return out
 
 
+# ---- every workload of the study, one method -------------------------------
+
+GRAPH_REPEATS = 5
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"), default=1)
+    except Exception:  # threadpoolctl missing: report the affinity set
+        return len(os.sched_getaffinity(0))
+
+
+def graph_time_us(call, est_us):
+    """Median per-call GPU time of ``call``: R calls captured in one HIP
+    graph, the graph replayed GRAPH_REPEATS times with HIP events around each
+    replay on the current stream (the stream the calls launch on).  Returns
+    (median_us, [per-call us of each replay], R)."""
+    R = int(min(200, max(4, 20000.0 / max(est_us, 1.0))))   # ~20 ms per replay
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(R):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(GRAPH_REPEATS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / R)
+    del g
+    return sorted(per)[len(per) // 2], [round(x, 3) for x in per], R
+
+
+def oracle_time_us(fn, one_core, min_runs=1, budget_s=10.0):
+    """Wall time of the oracle call ``fn``: one warm-up, then runs until
+    ``budget_s`` has passed (at least ``min_runs``); the median in us."""
+    from threadpoolctl import threadpool_limits
+    ctx = threadpool_limits(1) if one_core else None
+    try:
+        if ctx is not None:
+            ctx.__enter__()
+        fn()
+        ts, t0 = [], time.perf_counter()
+        while len(ts) < min_runs or (time.perf_counter() - t0 < budget_s and len(ts) < 200):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        return sorted(ts)[len(ts) // 2] * 1e6, len(ts)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+
+
+def fwd_bytes(B, H, Lq, Lk, d, esz, o_esz):
+    """Algorithmic HBM bytes of one forward: Q, K, V read, O and lse written."""
+    return B * H * ((Lq + 2 * Lk) * d * esz + Lq * d * o_esz + Lq * 4)
+
+
+def bwd_bytes(B, H, Lq, Lk, d, esz):
+    """Algorithmic HBM bytes of one backward: Q, K, V, O, dO and lse read,
+    dQ, dK, dV written."""
+    return B * H * ((3 * Lq + 4 * Lk) * d * esz + Lq * 4 + Lq * d * esz)
+
+
+def _entry(name, call, what, us, reps, R, fl, nbytes, peak_tflops, peak_name):
+    tf = fl / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    ai = fl / nbytes
+    ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return {
+        "workload": what, "call": call, "us": round(us, 3), "us_per_replay": reps,
+        "calls_per_graph": R, "replays": GRAPH_REPEATS, "stat": "median",
+        "algorithmic_flops": fl, "algorithmic_bytes": nbytes,
+        "tflops": round(tf, 2), "peak_tflops": peak_tflops, "peak": peak_name,
+        "frac_of_peak": round(tf / peak_tflops, 4),
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "flop_per_byte": round(ai, 1), "ridge_flop_per_byte": round(ridge, 1),
+        "bound": "mfma" if (ai > ridge and peak_name.startswith("bf16")) else
+                 ("valu" if ai > ridge else "hbm"),
+    }
+
+
+def bench_workloads(with_cpu):
+    """Every workload of the study through the C ABI (see the module notes)."""
+    import oracle
+    from workloads import sample_rows, to_f64, workload_inputs
+    dev = torch.device("cuda", 0)
+    out = {}
+    threads = _blas_threads()
+
+    def forward_case(wname, causal, label, est_us, one_core, rows=None):
+        w = WORKLOADS[wname]
+        q, k, v = workload_inputs(w, with_dO=False)
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
+        O = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+        call = lambda: fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=causal, out=O, lse=lse)
+        us, reps, R = graph_time_us(call, est_us)
+        fl, _ = flops(w.B, w.H, w.Lq, w.Lk, w.d, causal)
+        esz = 4 if w.dtype == "f32" else 2
+        e = _entry(label, "fa_fwd", f"forward {w.dtype} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} "
+                   f"{'causal' if causal else 'non-causal'}", us, reps, R, fl,
+                   fwd_bytes(w.B, w.H, w.Lq, w.Lk, w.d, esz, esz),
+                   PEAK_F32_VALU_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS,
+                   "fp32 vector" if w.dtype == "f32" else "bf16 dense matrix core")
+        if with_cpu:
+            qf, kf, vf = (to_f64(t) for t in (q, k, v))
+            if rows is None:
+                fn = lambda: oracle.attn_fwd(qf, kf, vf, w.scale, causal)
+                us_all, n_all = oracle_time_us(fn, False, budget_s=3.0)
+                cb = {"kind": "oracle", "all_cores": {"us": round(us_all, 1), "cores": threads,
+                                                      "runs": n_all},
+                      "sample": "the whole workload (fp64 numpy, full S per slice), median of runs"}
+                if one_core:
+                    us_1, n_1 = oracle_time_us(fn, True, budget_s=3.0)
+                    cb["one_core"] = {"us": round(us_1, 1), "cores": 1, "runs": n_1}
+                cb["gpu_speedup_vs_all_cores"] = round(us_all / us, 1)
+            else:
+                ridx = sample_rows(w.H, w.Lq, rows, w.seed, B=w.B).numpy()
+                fn = lambda: oracle.attn_fwd_rows(qf, kf, vf, w.scale, causal, ridx)
+                us_s, n_s = oracle_time_us(fn, False, budget_s=0.0)
+                pairs = sum(int(r) + 1 if causal else w.Lk for r in ridx.ravel())
+                fl_s = 4.0 * w.d * pairs
+                cb = {"kind": "oracle", "all_cores": {"us": round(us_s, 1), "cores": threads,
+                                                      "runs": n_s},
+                      "sample": f"{rows} seeded query rows per head, every head (fp64 numpy, "
+                                f"full rows over the visible keys): {fl_s:.3e} of {fl:.3e} FLOP",
+                      "tflops_on_sample": round(fl_s / (us_s * 1e-6) / 1e12, 5)}
+            e["cpu_baseline"] = cb
+        out[label] = e
+
+    def backward_case(wname, label, est_us, heads_budget_s):
+        w = WORKLOADS[wname]
+        q, k, v, do = workload_inputs(w, with_dO=True)
+        qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+        O, lse = fa.fa_fwd(qd, kd, vd, scale=w.scale, causal=True)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(qd.dtype, w.B, w.H, w.Lq, w.Lk, w.d),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: fa.fa_bwd(qd, kd, vd, O, dod, lse, scale=w.scale, causal=True, dq=dq, dk=dk,
+                                 dv=dv, workspace=ws)
+        us, reps, R = graph_time_us(call, est_us)
+        _, fl = flops(w.B, w.H, w.Lq, w.Lk, w.d, True)
+        e = _entry(label, "fa_bwd", f"backward bf16 B{w.B} H{w.H} L{w.Lq} d{w.d} causal "
+                   "(D statistic, dK/dV, dQ)", us, reps, R, fl,
+                   bwd_bytes(w.B, w.H, w.Lq, w.Lk, w.d, 2), PEAK_BF16_TFLOPS,
+                   "bf16 dense matrix core")
+        if with_cpu:
+            qf, kf, vf, dof = (to_f64(t) for t in (q, k, v, do))
+            n, t0 = 0, time.perf_counter()
+            while n < w.B * w.H:
+                b, h = divmod(n, w.H)
+                oracle.attn_bwd(qf[b:b + 1, h:h + 1], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1],
+                                dof[b:b + 1, h:h + 1], w.scale, True)
+                n += 1
+                if time.perf_counter() - t0 >= heads_budget_s:
+                    break
+            el = time.perf_counter() - t0
+            per_slice_us = el / n * 1e6
+            e["cpu_baseline"] = {
+                "kind": "oracle", "all_cores": {"us": round(per_slice_us * w.B * w.H, 1),
+                                                "cores": threads, "runs": 1},
+                "sample": f"{n} of {w.B * w.H} slices timed (backward, which recomputes the "
+                          f"forward; fp64 numpy, full S), {el:.1f} s wall, scaled to all slices",
+                "tflops": round(fl / w.B / w.H * n / el / 1e12, 5)}
+        out[label] = e
+
+    forward_case("fwd_f32_B1H1L128d64", False, "fwd_f32_B1H1L128d64", 10.0, True)
+    forward_case("fwd_bf16_B4H16L1024d64", False, "fwd_bf16_B4H16L1024d64_noncausal", 25.0, True)
+    forward_case("fwd_bf16_B4H16L1024d64", True, "fwd_bf16_B4H16L1024d64_causal", 15.0, True)
+    forward_case(BENCH_WORKLOAD, True, "fwd_bf16_B1H32L4096d128_causal", 130.0, False, rows=256)
+    forward_case("fwd_bf16_causal_B1H8L32768d128", True, "fwd_bf16_B1H8L32768d128_causal",
+                 2000.0, False, rows=256)
+    backward_case(BENCH_WORKLOAD, "bwd_bf16_B1H32L4096d128_causal", 450.0, 8.0)
+    backward_case("bwd_bf16_causal_B2H16L2048d128", "bwd_bf16_B2H16L2048d128_causal", 150.0, 8.0)
+    return out
+
+
+def measure_clock(step):
+    """Shader clock from a one-wave spin kernel that waits a fixed number of
+    clock cycles (torch.cuda._sleep), timed with HIP events: alone, and on a
+    second stream while ``step`` runs on the current one (then the spin wave
+    shares the chip with the attention kernels and sees their clock)."""
+    cycles = 40_000_000
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(cycles)
+    e1.record()
+    torch.cuda.synchronize()
+    idle_ghz = cycles / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The spin (~10 ms) starts while the first steps run; the steps queued
+    # after it keep the chip busy for ~2.5x its length.
+    for _ in range(4):
+        step()
+    with torch.cuda.stream(side):
+        f0.record()
+        torch.cuda._sleep(cycles // 2)
+        f1.record()
+    for _ in range(40):
+        step()
+    torch.cuda.synchronize()
+    load_ghz = (cycles // 2) / (f0.elapsed_time(f1) * 1e-3) / 1e9
+    return {"idle_ghz": round(idle_ghz, 3), "under_load_ghz": round(load_ghz, 3),
+            "method": "spin kernel of N shader-clock cycles (torch.cuda._sleep) timed with HIP "
+                      "events; under load it runs on a second stream beside the headline step",
+            "published_peak_clock_ghz": 2.4}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +591,19 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
 
+    # Five more blocks of the same K steps (untimed for value): the spread
+    # of the step time, reported as a median.
+    blocks = []
+    for _ in range(5):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(args.steps):
+            step()
+        b1.record()
+        torch.cuda.synchronize()
+        blocks.append(b0.elapsed_time(b1) / args.steps)
+    clock = measure_clock(step)
+
     f_fwd, f_bwd = flops(B, H, L, L, d, True)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     table = kernel_table(B, H, L, d)
@@ -395,7 +649,16 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_bytes": t["bytes"]},
         "cpu_baseline": None,
+        "repeats": {"blocks": 5, "steps_per_block": args.steps,
+                    "ms_per_step": [round(x, 4) for x in blocks],
+                    "median_ms_per_step": round(sorted(blocks)[2], 4),
+                    "median_tflops": round((f_fwd + f_bwd) / (sorted(blocks)[2] * 1e-3) / 1e12, 2)},
+        "clock": clock,
     }
+    try:
+        line["workloads"] = bench_workloads(not args.no_cpu_baseline)
+    except Exception as e:  # noqa: BLE001  (recorded instead of losing the main line)
+        line["workloads"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_decode:
         # Measured after the timed steps above; not part of value.  A failure
         # here is recorded in the line instead of losing the main measurement.

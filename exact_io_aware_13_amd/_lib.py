@@ -46,13 +46,14 @@ def _declare(lib):
     lib.fa_fwd_blocksparse.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, f32, i32, vp,
                                        i64, vp, vp, vp]
     lib.fa_bwd.restype = i32
-    lib.fa_bwd.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
+    lib.fa_bwd.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
                            vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_blocksparse.restype = i32
-    lib.fa_bwd_blocksparse.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32, i32,
-                                       vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_blocksparse.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                       f32, i32, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_prepare.restype = i32
-    lib.fa_bwd_prepare.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_prepare.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     lib.fa_bwd_dkdv.restype = i32
     lib.fa_bwd_dkdv.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, vp, vp,
                                 ctypes.c_size_t, vp]

@@ -136,17 +136,20 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
            workspace=None):
     """dQ, dK, dV through libfa's ``fa_bwd``.
 
-    o and lse are the forward's outputs (o in the input dtype), do the
-    gradient of o.  ``workspace`` (a uint8 device tensor) is allocated here
-    when not given.  Returns (dq, dk, dv) in the input dtype.
+    o and lse are the forward's outputs (o in the input dtype, or float32
+    beside bfloat16 inputs: the C call's o_dtype is o's dtype), do the
+    gradient of o in the input dtype.  ``workspace`` (a uint8 device tensor)
+    is allocated here when not given.  Returns (dq, dk, dv) in the input
+    dtype.
     """
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     dev = q.device
     _check_tensor("q", q, dev)
     for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
-                         ("o", o, (B, H, Lq, d)), ("do", do, (B, H, Lq, d))):
+                         ("do", do, (B, H, Lq, d))):
         _check_tensor(name, t, dev, q.dtype, shp)
+    _check_tensor("o", o, dev, None, (B, H, Lq, d))
     _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -160,9 +163,9 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, dev, torch.uint8)
     lib = _lib.load()
-    st = lib.fa_bwd(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
-                    _ptr(lse), float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
-                    _ptr(workspace), workspace.numel(), _stream(dev))
+    st = lib.fa_bwd(_code(q.dtype), _code(o.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
+                    _ptr(o), _ptr(do), _ptr(lse), float(scale), int(bool(causal)), _ptr(dq),
+                    _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(st)
     return dq, dk, dv
 
@@ -176,8 +179,9 @@ def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=False
     dev = q.device
     _check_tensor("q", q, dev)
     for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
-                         ("o", o, (B, H, Lq, d)), ("do", do, (B, H, Lq, d))):
+                         ("do", do, (B, H, Lq, d))):
         _check_tensor(name, t, dev, q.dtype, shp)
+    _check_tensor("o", o, dev, None, (B, H, Lq, d))
     _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
     nqb, nkb = -(-Lq // SPARSE_BLOCK), -(-Lk // SPARSE_BLOCK)
     if block_mask.dtype == torch.bool:
@@ -200,7 +204,7 @@ def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=False
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, dev, torch.uint8)
-    st = _lib.load().fa_bwd_blocksparse(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
+    st = _lib.load().fa_bwd_blocksparse(_code(q.dtype), _code(o.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v),
                                         _ptr(o), _ptr(do), _ptr(lse), float(scale),
                                         int(bool(causal)), _ptr(block_mask), slices, _ptr(dq),
                                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
@@ -223,15 +227,16 @@ def _bwd_shapes(q, k, v, do):
 def fa_bwd_prepare(o, do, lse, Lk, workspace):
     """Stage 1 of ``fa_bwd``: per-row statistics into ``workspace``.
 
-    ``Lk`` is the key length of the later stages (it sizes the checks).
+    ``do`` is in the input dtype, ``o`` in that dtype or float32.  ``Lk`` is
+    the key length of the later stages (it sizes the checks).
     """
     B, H, Lq, d = o.shape
     dev = o.device
     _check_tensor("o", o, dev)
-    _check_tensor("do", do, dev, o.dtype, o.shape)
+    _check_tensor("do", do, dev, None, o.shape)
     _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
     _check_tensor("workspace", workspace, dev, torch.uint8)
-    st = _lib.load().fa_bwd_prepare(_code(o.dtype), B, H, Lq, Lk, d, _ptr(o), _ptr(do), _ptr(lse),
+    st = _lib.load().fa_bwd_prepare(_code(do.dtype), _code(o.dtype), B, H, Lq, Lk, d, _ptr(o), _ptr(do), _ptr(lse),
                                     _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(st)
 

@@ -21,15 +21,19 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Shape checks shared by forward, backward and workspace sizing.  Slices get
 // one tile of slack so that in-kernel offsets of the last (ragged) tile stay
 // representable.
+// Every size is bounded before it enters a product, so no product below can
+// overflow int64 whatever the caller passes.
 fa_status check_shape(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d) {
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d <= 0) return FA_ERR_SHAPE;
-  if (B * H > 0 && Lq > 0 && Lk == 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B > INT32_MAX || H > INT32_MAX || Lq > INT32_MAX || Lk > INT32_MAX) return FA_ERR_SHAPE;
+  // All four are now below 2^31, so the products below stay below 2^62.
+  if (B * H > INT32_MAX) return FA_ERR_SHAPE;
+  if (B * H > 0 && Lq > 0 && Lk == 0) return FA_ERR_SHAPE;
   const int64_t slack = 256;
   const int64_t esz = 4;  // fp32 outputs and accumulators bound every path
   if ((Lq + slack) * d * esz >= kMaxSliceBytes || (Lk + slack) * d * esz >= kMaxSliceBytes)
     return FA_ERR_SHAPE;
-  if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX) return FA_ERR_SHAPE;
   const int64_t bh = B * H;
   // Row counts bound the grids of the row-wise helper kernels.
   if (bh * Lq > (int64_t(1) << 34) || bh * Lk > (int64_t(1) << 34)) return FA_ERR_SHAPE;
@@ -142,14 +146,16 @@ namespace {
 
 // Shared by fa_bwd and its three stages: validates exactly the pointers the
 // requested stages touch, then enqueues those stages.
-fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq,
-                     int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
+fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H,
+                     int64_t Lq, int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
                      const void* O, const void* dO, const float* lse, float scale, int causal,
                      void* dQ, void* dK, void* dV, const void* workspace, size_t workspace_bytes,
                      hipStream_t stream, const uint8_t* block_mask = nullptr,
                      int64_t mask_slices = 0) {
-  if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
   if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  // O is in the input dtype, or fp32 beside bf16 inputs (fa_fwd's outputs).
+  if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   const bool has_q = B * H * Lq > 0, has_k = B * H * Lk > 0;
   if (!has_q && !has_k) return FA_OK;
   const bool pre = stages & fa::kBwdPrepare, kv = stages & fa::kBwdDkDv, dq = stages & fa::kBwdDq;
@@ -186,6 +192,7 @@ fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, i
   a.d = (int)d;
   a.scale = scale;
   a.causal = causal != 0;
+  a.o_f32 = o_dtype == FA_F32;
   if (block_mask) {
     a.block_mask = block_mask;
     a.nqb = (int)cdiv(Lq, fa::kSparseBlock);
@@ -207,35 +214,38 @@ fa_status bwd_stages(unsigned stages, fa_dtype in_dtype, int64_t B, int64_t H, i
 
 extern "C" {
 
-fa_status fa_bwd(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
-                 const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                 const float* lse, float scale, int causal, void* dQ, void* dK, void* dV,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_stages(fa::kBwdAll, in_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale, causal,
-                    dQ, dK, dV, workspace, workspace_bytes, stream);
+fa_status fa_bwd(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H, int64_t Lq,
+                 int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse, float scale, int causal,
+                 void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return bwd_stages(fa::kBwdAll, in_dtype, o_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale,
+                    causal, dQ, dK, dV, workspace, workspace_bytes, stream);
 }
 
-fa_status fa_bwd_prepare(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                         int64_t d, const void* O, const void* dO, const float* lse,
+fa_status fa_bwd_prepare(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H, int64_t Lq,
+                         int64_t Lk, int64_t d, const void* O, const void* dO, const float* lse,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_stages(fa::kBwdPrepare, in_dtype, B, H, Lq, Lk, d, nullptr, nullptr, nullptr, O, dO,
-                    lse, 1.f, 0, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+  return bwd_stages(fa::kBwdPrepare, in_dtype, o_dtype, B, H, Lq, Lk, d, nullptr, nullptr, nullptr,
+                    O, dO, lse, 1.f, 0, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                    stream);
 }
 
 fa_status fa_bwd_dkdv(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                       const void* Q, const void* K, const void* V, const void* dO, float scale,
                       int causal, void* dK, void* dV, const void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  return bwd_stages(fa::kBwdDkDv, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO, nullptr, scale,
-                    causal, nullptr, dK, dV, workspace, workspace_bytes, stream);
+  return bwd_stages(fa::kBwdDkDv, in_dtype, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO,
+                    nullptr, scale, causal, nullptr, dK, dV, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_bwd_dq(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                     const void* Q, const void* K, const void* V, const void* dO, float scale,
                     int causal, void* dQ, const void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  return bwd_stages(fa::kBwdDq, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO, nullptr, scale,
-                    causal, dQ, nullptr, nullptr, workspace, workspace_bytes, stream);
+  return bwd_stages(fa::kBwdDq, in_dtype, in_dtype, B, H, Lq, Lk, d, Q, K, V, nullptr, dO,
+                    nullptr, scale, causal, dQ, nullptr, nullptr, workspace, workspace_bytes,
+                    stream);
 }
 
 }  // extern "C"
@@ -359,21 +369,22 @@ fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype, int64_t B, int64_t H, int64_t
 
 extern "C" {
 
-fa_status fa_bwd_blocksparse(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                             int64_t d, const void* Q, const void* K, const void* V, const void* O,
+fa_status fa_bwd_blocksparse(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H,
+                             int64_t Lq, int64_t Lk, int64_t d, const void* Q, const void* K, const void* V, const void* O,
                              const void* dO, const float* lse, float scale, int causal,
                              const uint8_t* block_mask, int64_t mask_slices, void* dQ, void* dK,
                              void* dV, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  if (!valid_dtype(in_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
   if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
   if (in_dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (mask_slices != 1 && mask_slices != B * H) return FA_ERR_ARG;
   const int64_t nqb = cdiv(Lq, fa::kSparseBlock), nkb = cdiv(Lk, fa::kSparseBlock);
   if (nkb > fa::kSparseMaxKeyBlocks || nqb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
   if (B * H * (Lq + Lk) > 0 && !block_mask) return FA_ERR_NULL;
-  return bwd_stages(fa::kBwdAll, in_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale, causal, dQ,
-                    dK, dV, workspace, workspace_bytes, stream, block_mask, mask_slices);
+  return bwd_stages(fa::kBwdAll, in_dtype, o_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale,
+                    causal, dQ, dK, dV, workspace, workspace_bytes, stream, block_mask,
+                    mask_slices);
 }
 
 }  // extern "C"

@@ -68,9 +68,11 @@ namespace {
 // ---------------------------------------------------------------------------
 // 1. D statistic (stored negated) and base-2 lse
 // ---------------------------------------------------------------------------
-template <int D>
+// O_F32: O is the fp32 output of the forward's fp32-output variant (dO stays
+// bf16); D is summed in fp32 either way.
+template <int D, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
-    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+    const void* __restrict__ O, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse, float* __restrict__ Dvec, float* __restrict__ lse2,
     int64_t rows) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements each
@@ -79,10 +81,26 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
   const int c = wi_id() % LPR;
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * D + c * 8);
     const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c * 8);
+    float o8[8];
+    if constexpr (O_F32) {
+      const f32x4* op = reinterpret_cast<const f32x4*>(static_cast<const float*>(O) + row * D + c * 8);
+      const f32x4 a = op[0], b = op[1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc += bf16_lo(o[i]) * bf16_lo(g[i]) + bf16_hi(o[i]) * bf16_hi(g[i]);
+      for (int i = 0; i < 4; ++i) {
+        o8[i] = a[i];
+        o8[4 + i] = b[i];
+      }
+    } else {
+      const u32x4 o = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(O) + row * D + c * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o8[2 * i] = bf16_lo(o[i]);
+        o8[2 * i + 1] = bf16_hi(o[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += o8[2 * i] * bf16_lo(g[i]) + o8[2 * i + 1] * bf16_hi(g[i]);
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -1008,9 +1026,13 @@ hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Lq;
   if ((stages & kBwdPrepare) && rows > 0) {
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
-                       0, stream, static_cast<const uint16_t*>(a.O),
-                       static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+    if (a.o_f32)
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, true>), grid, dim3(256), 0, stream, a.O,
+                         static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
+    else
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a.O,
+                         static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
   }
   if (a.block_mask) {
     if (a.causal) launch_main<D, true, true>(a, stages, stream);

@@ -43,6 +43,7 @@ struct BwdArgs {
   int BH, Lq, Lk, d;
   float scale;
   bool causal;
+  bool o_f32 = false;  // O is fp32 (beside bf16 inputs); else the input dtype
   // Block-sparse backward (bf16 only), as in FwdArgs; NULL for the dense one.
   const uint8_t* block_mask = nullptr;
   int bm_stride = 0, nqb = 0, nkb = 0;

@@ -149,8 +149,14 @@ FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
  * Equivalent to fa_bwd_prepare, then fa_bwd_dkdv and fa_bwd_dq on the same
  * stream.  No atomics: every gradient row is summed in a fixed order by one
  * workgroup, so results are bitwise reproducible.
- *   in_dtype   dtype of Q, K, V, O, dO, dQ, dK, dV (O and dO must be in
- *              the input dtype; the fp32-output forward is a diagnostic).
+ *   in_dtype   dtype of Q, K, V, dO, dQ, dK, dV.
+ *   o_dtype    dtype of O, as the forward wrote it: equal to in_dtype, or
+ *              FA_F32 with bf16 inputs (fa_fwd's fp32-output variant).  O
+ *              enters only D = rowsum(dO * O), which is formed in fp32 from
+ *              whichever O is given.  dO stays in in_dtype: it is an operand
+ *              of the matrix products.  FA_F32 inputs with bf16 O return
+ *              FA_ERR_UNSUPPORTED; a value that is not an fa_dtype returns
+ *              FA_ERR_ARG.
  *   lse        the forward's [B,H,Lq] output.
  *   scale, causal  the values the forward was called with.
  *   dQ         [B,H,Lq,d], dK, dV: [B,H,Lk,d], written.
@@ -159,7 +165,7 @@ FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
  *              scratch afterwards.  Concurrent calls need separate
  *              workspaces.
  */
-FA_API fa_status fa_bwd(fa_dtype in_dtype,
+FA_API fa_status fa_bwd(fa_dtype in_dtype, fa_dtype o_dtype,
                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                  const void* Q, const void* K, const void* V,
                  const void* O, const void* dO, const float* lse,
@@ -175,10 +181,11 @@ FA_API fa_status fa_bwd(fa_dtype in_dtype,
  * stage validates only the pointers it uses.
  *
  * fa_bwd_prepare writes the per-row statistics (D and lse in base 2) into
- * `workspace`.  It must complete before fa_bwd_dkdv or
- * fa_bwd_dq starts reading that workspace (same stream, or an event).
+ * `workspace`; it reads O in o_dtype (as for fa_bwd).  It must complete
+ * before fa_bwd_dkdv or fa_bwd_dq starts reading that workspace (same
+ * stream, or an event).
  */
-FA_API fa_status fa_bwd_prepare(fa_dtype in_dtype,
+FA_API fa_status fa_bwd_prepare(fa_dtype in_dtype, fa_dtype o_dtype,
                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                  const void* O, const void* dO, const float* lse,
                  void* workspace, size_t workspace_bytes,
@@ -288,13 +295,13 @@ FA_API fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype,
  * chain rule through the masked definition (P is zero outside the kept
  * pairs; a row that sees no key contributes nothing).  lse and O must be
  * fa_fwd_blocksparse's outputs (rows that see no key: O = 0, lse = -inf).
- * Workspace, layouts and status codes as for fa_bwd; supported: in_dtype
+ * o_dtype, workspace, layouts and status codes as for fa_bwd; supported: in_dtype
  * FA_BF16, d in {64, 128}, ceil(Lq/128) and ceil(Lk/128) <= 4096 (else
  * FA_ERR_UNSUPPORTED).  The key-side kernel visits only the query blocks
  * that see its key block; the query side visits the key blocks either of a
  * workgroup's two 128-row blocks sees.
  */
-FA_API fa_status fa_bwd_blocksparse(fa_dtype in_dtype,
+FA_API fa_status fa_bwd_blocksparse(fa_dtype in_dtype, fa_dtype o_dtype,
                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                  const void* Q, const void* K, const void* V,
                  const void* O, const void* dO, const float* lse,

@@ -30,13 +30,14 @@ def _fwd(lib, in_dt=BF16, out_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, Q=P, K=P, 
     return lib.fa_fwd(in_dt, out_dt, B, H, Lq, Lk, d, Q, K, V, scale, causal, O, lse, None)
 
 
-def _bwd(lib, in_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125, causal=1,
-         ws=P, ws_bytes=None):
+def _bwd(lib, in_dt=BF16, o_dt=None, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125,
+         causal=1, ws=P, ws_bytes=None):
     p = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dQ=P, dK=P, dV=P)
     p.update(ptrs or {})
+    o_dt = in_dt if o_dt is None else o_dt
     if ws_bytes is None:
         ws_bytes = lib.fa_bwd_workspace_bytes(in_dt, B, H, Lq, Lk, d)
-    return lib.fa_bwd(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["O"], p["dO"], p["lse"],
+    return lib.fa_bwd(in_dt, o_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["O"], p["dO"], p["lse"],
                       scale, causal, p["dQ"], p["dK"], p["dV"], ws, ws_bytes, None)
 
 
@@ -69,6 +70,10 @@ def test_status_strings(lib):
     (dict(scale=float("inf")), ARG),
     (dict(B=-1), SHAPE), (dict(Lq=-3), SHAPE), (dict(d=0), SHAPE), (dict(Lk=0), SHAPE),
     (dict(Lq=1 << 24), SHAPE), (dict(Lk=1 << 24), SHAPE), (dict(B=1 << 20, H=1 << 20), SHAPE),
+    # Sizes whose products overflow int64 are rejected before any product.
+    (dict(B=1 << 40, H=1 << 40), SHAPE), (dict(B=1 << 62, H=4), SHAPE),
+    (dict(Lq=2 ** 63 - 1), SHAPE), (dict(Lk=2 ** 63 - 1), SHAPE),
+    (dict(B=2 ** 63 - 1, H=2 ** 63 - 1, Lq=2 ** 63 - 1, Lk=2 ** 63 - 1), SHAPE),
     (dict(d=96), UNSUP), (dict(d=32), UNSUP), (dict(d=256), UNSUP),
     (dict(in_dt=F32, out_dt=BF16), UNSUP),
     (dict(Q=None), NULL), (dict(K=None), NULL), (dict(V=None), NULL), (dict(O=None), NULL),
@@ -87,7 +92,10 @@ def test_fwd_empty_is_ok_and_touches_nothing(lib, kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(in_dt=3), ARG), (dict(scale=float("nan")), ARG),
+    # O's dtype: an unknown value, and bf16 O beside fp32 inputs.
+    (dict(o_dt=2), ARG), (dict(o_dt=-1), ARG), (dict(in_dt=F32, o_dt=BF16), UNSUP),
     (dict(Lk=0), SHAPE), (dict(d=80), UNSUP),
+    (dict(B=1 << 40, H=1 << 40), SHAPE), (dict(Lq=2 ** 63 - 1, Lk=2 ** 63 - 1), SHAPE),
     (dict(ptrs=dict(dO=None)), NULL), (dict(ptrs=dict(lse=None)), NULL),
     (dict(ptrs=dict(dV=None)), NULL), (dict(ptrs=dict(dQ=None)), NULL),
     (dict(ptrs=dict(dK=P + 8)), ALIGN), (dict(ptrs=dict(O=P + 2)), ALIGN),
@@ -97,14 +105,15 @@ def test_bwd_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
-def _stage(lib, name, in_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125,
-           causal=1, ws=P, ws_bytes=None):
+def _stage(lib, name, in_dt=BF16, o_dt=None, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None,
+           scale=0.125, causal=1, ws=P, ws_bytes=None):
     p = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dQ=P, dK=P, dV=P)
     p.update(ptrs or {})
+    o_dt = in_dt if o_dt is None else o_dt
     if ws_bytes is None:
         ws_bytes = lib.fa_bwd_workspace_bytes(in_dt, B, H, Lq, Lk, d)
     if name == "prepare":
-        return lib.fa_bwd_prepare(in_dt, B, H, Lq, Lk, d, p["O"], p["dO"], p["lse"], ws, ws_bytes,
+        return lib.fa_bwd_prepare(in_dt, o_dt, B, H, Lq, Lk, d, p["O"], p["dO"], p["lse"], ws, ws_bytes,
                                   None)
     if name == "dkdv":
         return lib.fa_bwd_dkdv(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["dO"], scale,
@@ -115,6 +124,7 @@ def _stage(lib, name, in_dt=BF16, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scal
 
 @pytest.mark.parametrize("name,kw,status", [
     ("prepare", dict(in_dt=4), ARG), ("prepare", dict(Lk=0), SHAPE), ("prepare", dict(d=48), UNSUP),
+    ("prepare", dict(o_dt=7), ARG), ("prepare", dict(in_dt=F32, o_dt=BF16), UNSUP),
     ("prepare", dict(ptrs=dict(O=None)), NULL), ("prepare", dict(ptrs=dict(lse=None)), NULL),
     ("prepare", dict(ptrs=dict(dO=P + 2)), ALIGN), ("prepare", dict(ws=None), WS),
     ("prepare", dict(ws_bytes=8), WS),
@@ -252,9 +262,11 @@ def test_blocksparse_accepts_per_slice_mask_count(lib):
 def test_bwd_blocksparse_rejects(lib):
     ws = lib.fa_bwd_workspace_bytes(BF16, 1, 2, 300, 300, 128)
     call = lambda **kw: lib.fa_bwd_blocksparse(
-        kw.get("dt", BF16), 1, 2, 300, kw.get("Lk", 300), 128, P, P, P, P, P, P, 0.1, 1,
+        kw.get("dt", BF16), kw.get("o_dt", kw.get("dt", BF16)), 1, 2, 300, kw.get("Lk", 300), 128, P, P, P, P, P, P, 0.1, 1,
         kw.get("mask", P + 1), kw.get("slices", 1), P, P, P, P, kw.get("ws", ws), None)
     assert call(dt=F32) == UNSUP
+    assert call(o_dt=5) == ARG
+    assert call(dt=F32, o_dt=BF16) == UNSUP
     assert call(slices=3) == ARG
     assert call(mask=None) == NULL
     assert call(ws=8) == WS

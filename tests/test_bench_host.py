@@ -83,3 +83,27 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_workload_byte_counts(bench):
+    # Forward: Q, K, V in (element size esz), O out (o_esz), lse out (fp32).
+    assert bench.fwd_bytes(4, 16, 1024, 1024, 64, 2, 2) == 4 * 16 * (4 * 1024 * 64 * 2 + 1024 * 4)
+    assert bench.fwd_bytes(1, 1, 128, 128, 64, 4, 4) == 4 * 128 * 64 * 4 + 128 * 4 == 131_584
+    # Longer keys than queries: K and V scale with Lk, Q and O with Lq.
+    assert bench.fwd_bytes(1, 1, 10, 30, 64, 2, 4) == 10 * 64 * 2 + 2 * 30 * 64 * 2 + 10 * 64 * 4 + 40
+    # Backward: Q, K, V, O, dO, lse in; dQ, dK, dV out.
+    t = 2 * 16 * 2048 * 128 * 2
+    assert bench.bwd_bytes(2, 16, 2048, 2048, 128, 2) == 8 * t + 2 * 16 * 2048 * 4
+
+
+def test_workload_entry_arithmetic(bench):
+    # 1.3744e11 FLOP in 110 us is 1249.5 TFLOP/s, half the 2500 peak; with
+    # 134.7 MB the byte rate is 1225 GB/s and the intensity above the ridge.
+    e = bench._entry("x", "fa_fwd", "w", 110.0, [110.0], 10, 2 ** 37, 134_742_016, 2500.0,
+                     "bf16 dense matrix core")
+    assert abs(e["tflops"] - 2 ** 37 / 110e-6 / 1e12) < 0.01
+    assert abs(e["frac_of_peak"] - 2 ** 37 / 110e-6 / 1e12 / 2500.0) < 1e-4
+    assert abs(e["hbm_gbs"] - 134_742_016 / 110e-6 / 1e9) < 0.1
+    assert e["ridge_flop_per_byte"] == 312.5 and e["bound"] == "mfma"
+    low = bench._entry("y", "fa_fwd", "w", 10.0, [10.0], 10, 1e6, 1e6, 2500.0, "bf16 dense matrix core")
+    assert low["bound"] == "hbm"

@@ -141,3 +141,64 @@ def test_stages_equal_fused_call_across_two_streams(dtype):
     dk, dv = fa.fa_bwd_dkdv(qd, kd, vd, dod, ws, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+
+
+def _gpu_grads_f32_out(q, k, v, do, scale, causal):
+    # The forward's fp32-output variant, whose O goes into the backward as
+    # fp32 (o_dtype = FA_F32); dO stays bf16.
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    O, lse = fa.fa_fwd(qd, kd, vd, scale=scale, causal=causal, out_dtype=torch.float32)
+    assert O.dtype == torch.float32
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, O, dod, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return f64(dq), f64(dk), f64(dv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 64), (1, 2, 200, 333, 128), (2, 3, 129, 129, 64),
+                                   (1, 2, 300, 17, 128), (2, 2, 256, 256, 128)],
+                         ids=lambda s: "B{}H{}Lq{}Lk{}d{}".format(*s))
+def test_bf16_inputs_fp32_output_backward(shape, causal):
+    B, H, Lq, Lk, d = shape
+    q, k, v, do = make_inputs(B, H, Lq, Lk, d, "bf16", seed=5 * Lq + Lk + d, with_dO=True)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"bwd bf16 with fp32 O {shape} causal={causal}")
+    got = _gpu_grads_f32_out(q, k, v, do, scale, causal)
+    ref = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), scale, causal)
+    _assert_grads(got, ref, BF16_GRAD_REL, f"fp32 O {shape} causal={causal}")
+
+
+def test_backward_workload_fp32_output_every_head():
+    # B2 H16 L2048 d128 causal with the forward's fp32 O fed to the backward.
+    w = WORKLOADS["bwd_bf16_causal_B2H16L2048d128"]
+    q, k, v, do = workload_inputs(w)
+    announce(f"bwd {w.name} fp32 O")
+    got = _gpu_grads_f32_out(q, k, v, do, w.scale, True)
+    ref = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), w.scale, True)
+    _assert_grads(got, ref, BF16_GRAD_REL, w.name + " fp32 O")
+
+
+def test_fp32_output_statistics_only_differ_through_o():
+    # fa_bwd_prepare with fp32 O reads the same dO and lse; only D differs,
+    # and by no more than the bf16 rounding of O can move it.
+    q, k, v, do = make_inputs(1, 2, 300, 300, 128, "bf16", seed=31, with_dO=True)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    announce("bwd prepare fp32 O vs bf16 O")
+    O32, lse = fa.fa_fwd(qd, kd, vd, causal=True, out_dtype=torch.float32)
+    nbytes = fa.fa_bwd_workspace_bytes(torch.bfloat16, 1, 2, 300, 300, 128)
+    ws32 = torch.empty(nbytes, dtype=torch.uint8, device=qd.device)
+    ws16 = torch.empty(nbytes, dtype=torch.uint8, device=qd.device)
+    fa.fa_bwd_prepare(O32, dod, lse, 300, ws32)
+    fa.fa_bwd_prepare(O32.to(torch.bfloat16), dod, lse, 300, ws16)
+    torch.cuda.synchronize()
+    rows = 2 * 300
+    stat = -(-rows * 4 // 256) * 256
+    d32 = ws32[:rows * 4].view(torch.float32).double().cpu()
+    d16 = ws16[:rows * 4].view(torch.float32).double().cpu()
+    l32 = ws32[stat:stat + rows * 4].view(torch.float32)
+    l16 = ws16[stat:stat + rows * 4].view(torch.float32)
+    assert torch.equal(l32, l16)
+    # D = -rowsum(dO * O) in fp64 from the fp32 O (the bf16 path stores -D).
+    d_ref = -(f64(do).reshape(rows, 128) * f64(O32).reshape(rows, 128)).sum(axis=1)
+    assert np.abs(d32.numpy() - d_ref).max() <= 1e-4 * max(1.0, np.abs(d_ref).max())
+    assert not torch.equal(d32, d16)
