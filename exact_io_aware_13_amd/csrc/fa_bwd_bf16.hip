@@ -669,6 +669,16 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     win0 = lane < nlist ? klist[lane] : 0u;
     win1 = 64 + lane < nlist ? klist[64 + lane] : 0u;
   }
+  // This wave's own trip count (the forward's rule): under a causal mask
+  // its rows see no key past tile (qw0 + 32 RB - 1) / BC, and rows all past
+  // Lq compute nothing that is kept.  Past it the wave only issues its share
+  // of the loads and joins the barriers; block-sparse workgroups run their
+  // list with every wave.
+  int nkt_w = nkt;
+  if constexpr (!SPARSE) {
+    if (CAUSAL) nkt_w = min(nkt, (qw0 + 32 * T::RB - 1) / T::BC + 1);
+    if (qw0 >= Lq) nkt_w = 1;
+  }
   auto entry_at = [&](int j) __attribute__((always_inline)) -> unsigned {
     const int e = j / TPB - wbase;
     const unsigned src = e < 64 ? win0 : win1;
@@ -947,7 +957,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   // the register allocator move the accumulators around every round), then
   // up to three more.
   int j = 1;
-  for (; j + 3 < nkt; j += 4) {
+  for (; j + 3 < nkt_w; j += 4) {
     window_for(j + 5);  // this round fetches up to tile j + 5
     iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
     iter(IC<2>{}, std::false_type{}, j + 1, dskB, dskA);
@@ -955,16 +965,18 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
     iter(IC<0>{}, std::false_type{}, j + 3, dskB, dskA);
   }
   window_for(j + 4);
-  if (j < nkt) {
+  if (j < nkt_w) {
     iter(IC<1>{}, std::false_type{}, j, dskA, dskB);
-    if (j + 1 < nkt) {
+    if (j + 1 < nkt_w) {
       iter(IC<2>{}, std::false_type{}, j + 1, dskB, dskA);
-      if (j + 2 < nkt) iter(IC<3>{}, std::false_type{}, j + 2, dskA, dskB);
+      if (j + 2 < nkt_w) iter(IC<3>{}, std::false_type{}, j + 2, dskA, dskB);
     }
   }
 
-  // ---- dQ^T of the last tile -------------------------------------------------------
-  wait_vm<0>();
+  // ---- dQ^T of the wave's last tile ------------------------------------------------
+  // K[nkt_w-1] was read by this wave's own last iteration; its slot is
+  // refilled only in iteration nkt_w+1, after the next barrier.
+  if (nkt_w == nkt) wait_vm<0>();
   auto last_dq = [&](const char* kb_, const unsigned (&ds)[T::RB][T::NKB][8])
                      __attribute__((always_inline)) {
     static_for<0, T::NT>([&](auto Fc) __attribute__((always_inline)) {
@@ -972,11 +984,33 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
       static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) { dq_product(a, ds, Fc, RBc); });
     });
   };
-  switch ((nkt - 1) & 3) {
+  switch ((nkt_w - 1) & 3) {
     case 0: last_dq(K0, dskA); break;
     case 1: last_dq(K1, dskB); break;
     case 2: last_dq(K2, dskA); break;
     default: last_dq(K3, dskB); break;
+  }
+  // Iterations nkt_w..nkt-1 without products: the same loads into the same
+  // slots, the same waits and barriers as the waves that still compute.
+  for (int jd = nkt_w; jd < nkt; ++jd) {
+    const int t = tile_at(min(jd + 2, nkt - 1));
+    const int sl = (jd + 2) & 3;
+    char* kd = sl == 0 ? K0 : sl == 1 ? K1 : sl == 2 ? K2 : K3;
+    char* vd = sl == 0 ? V0 : sl == 1 ? V1 : sl == 2 ? V2 : V3;
+    static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (lds_void*)(kd + w * T::LOADS * 1024), 16,
+          (uint32_t)(t * T::TILEB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    });
+    static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (lds_void*)(vd + w * T::LOADS * 1024), 16,
+          (uint32_t)(t * T::TILEB + fetch_off[i] - i * 1024), 0, i * 1024, 0);
+    });
+    wait_vm<2 * T::LOADS>();
+    block_barrier();
   }
   }  // !SPARSE || nkt > 0
   wait_vm<0>();  // the loads of the tiles past the last one

@@ -216,6 +216,18 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
     win0 = lane < nlist ? tlist[lane] : 0u;
     win1 = 64 + lane < nlist ? tlist[64 + lane] : 0u;
   }
+  // This wave's own trip count (after the block-sparse list has set nkt):
+  // under a causal mask its rows see no key past tile (qw0 + 32 RB - 1) /
+  // BC, and a wave whose rows all lie past Lq has nothing to compute (its
+  // stores are dropped).  Tiles past it are not multiplied; the wave still
+  // issues its share of every tile's loads and joins every barrier (see the
+  // drain after the main loop).  The block-sparse workgroup runs its list
+  // with every wave.
+  int nkt_w = nkt;
+  if constexpr (!SPARSE) {
+    if (CAUSAL) nkt_w = min(nkt, (qw0 + 32 * T::RB - 1) / T::BC + 1);
+    if (qw0 >= Lq) nkt_w = 1;
+  }
   // Key tile of loop position j (the window must hold entry j / TPB).
   auto tile_at = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) {
@@ -427,12 +439,6 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
 
     float rs[T::RB][4], tsum[T::RB];
     float xg[T::NGROUP][4];  // probability groups in flight between stages
-#pragma unroll
-    for (int rb = 0; rb < T::RB; ++rb) {
-      tsum[rb] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[rb][i] = 0.f;
-    }
     // Vector-ALU work placed after the matrix-product slots: groups of 4
     // probabilities, each moving through three stages on consecutive slots
     // (FMA, exp2, pack and sum), so no instruction waits right behind its
@@ -457,7 +463,11 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
         } else {
           pk_cur[rb][kb2][r0 / 2] = pack_bf16x2(xg[g][0], xg[g][1]);
           pk_cur[rb][kb2][r0 / 2 + 1] = pack_bf16x2(xg[g][2], xg[g][3]);
-          rs[rb][eg & 3] += (xg[g][0] + xg[g][1]) + (xg[g][2] + xg[g][3]);
+          // The first group of each partial sum assigns it (an fp add of 0
+          // is not folded away and would cost an instruction).
+          const float gs = (xg[g][0] + xg[g][1]) + (xg[g][2] + xg[g][3]);
+          if constexpr (eg < 4) rs[rb][eg & 3] = gs;
+          else rs[rb][eg & 3] += gs;
           pin(pk_cur[rb][kb2][r0 / 2]);
           pin(pk_cur[rb][kb2][r0 / 2 + 1]);
           pin(rs[rb][eg & 3]);
@@ -550,7 +560,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+        float sum[4];
 #pragma unroll
         for (int kb2 = 0; kb2 < T::NKB; ++kb2)
 #pragma unroll
@@ -561,7 +571,8 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
               x[e] = fast_exp2(__builtin_fmaf(s_cur[rb][kb2][4 * q4 + e], c, -m_new));
             pk_cur[rb][kb2][2 * q4] = pack_bf16x2(x[0], x[1]);
             pk_cur[rb][kb2][2 * q4 + 1] = pack_bf16x2(x[2], x[3]);
-            sum[q4] += (x[0] + x[1]) + (x[2] + x[3]);
+            const float gs = (x[0] + x[1]) + (x[2] + x[3]);
+            sum[q4] = kb2 == 0 ? gs : sum[q4] + gs;
           }
         tsum[rb] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
       }
@@ -598,28 +609,50 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB);
   // Four iterations per trip (j = 1..4 mod 4) as one straight-line chain, so
   // ring slots and register roles are compile-time in every body.
-  for (int j = 1; j < nkt; j += 4) {
+  for (int j = 1; j < nkt_w; j += 4) {
     window_for(min(j + 7, nkt - 1));  // this trip fetches up to tile j + 7
     iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA);
-    if (j + 1 >= nkt) break;
+    if (j + 1 >= nkt_w) break;
     iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB);
-    if (j + 2 >= nkt) break;
+    if (j + 2 >= nkt_w) break;
     iter(IC<3>{}, std::false_type{}, j + 2, sB, sA, pB, pA);
-    if (j + 3 >= nkt) break;
+    if (j + 3 >= nkt_w) break;
     iter(IC<0>{}, std::false_type{}, j + 3, sA, sB, pA, pB);
   }
 
-  // Value product of the last tile: P(nkt-1) is in pB when nkt-1 is even.
-  wait_vm<0>();
-  block_barrier();
-  {
-    const unsigned(&plast)[T::RB][T::NKB][8] = ((nkt - 1) & 1) ? pA : pB;
-    switch ((nkt - 1) & 3) {
+  // Value product of the wave's last tile: P(nkt_w-1) is in pB when nkt_w-1
+  // is even.
+  auto last_value = [&]() __attribute__((always_inline)) {
+    const unsigned(&plast)[T::RB][T::NKB][8] = ((nkt_w - 1) & 1) ? pA : pB;
+    switch ((nkt_w - 1) & 3) {
       case 0: value_tile(V0, plast); break;
       case 1: value_tile(V1, plast); break;
       case 2: value_tile(V2, plast); break;
       default: value_tile(V3, plast); break;
     }
+  };
+  if (nkt_w == nkt) {
+    wait_vm<0>();
+    block_barrier();
+    last_value();
+  } else {
+    // V[nkt_w-1] landed before the barrier that closed iteration nkt_w-1,
+    // and its slot is refilled only in iteration nkt_w+1, after the next
+    // barrier: read it now.  Then iterations nkt_w..nkt-1 without products:
+    // the same loads into the same slots, the same waits and barriers as
+    // the waves that still compute, and the final barrier they take before
+    // their last value product.
+    last_value();
+    for (int j = nkt_w; j < nkt; ++j) {
+      char* ks = (j & 3) == 0 ? K0 : (j & 3) == 1 ? K1 : (j & 3) == 2 ? K2 : K3;
+      char* vs = (j & 3) == 0 ? V2 : (j & 3) == 1 ? V3 : (j & 3) == 2 ? V0 : V1;
+      fetch(rk, j + 4, ks);
+      fetch(rv, j + 2, vs);
+      wait_vm<4 * T::LOADS>();
+      block_barrier();
+    }
+    wait_vm<0>();
+    block_barrier();
   }
   }  // !SPARSE || nkt > 0
 
