@@ -903,6 +903,12 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
       });
     };
     auto run = [&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      // Issue priority falls 3, 2, 1, 0 over the quarters of the
+      // iteration's products, so the wave of a SIMD pair that runs ahead
+      // yields contested matrix-core slots to the one behind (as in the
+      // forward).
+      if constexpr ((4 * i) % NALL == 0) __builtin_amdgcn_s_setprio(3 - (4 * i) / NALL);
       product(Ic);
       slot(Ic);
       __builtin_amdgcn_sched_barrier(0);

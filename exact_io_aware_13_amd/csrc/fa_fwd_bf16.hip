@@ -134,6 +134,10 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = FwdTile<D, MODE != 0>;
   constexpr bool SPARSE = MODE == 2;
+  // Quarter priorities within each iteration (see the product loop): for
+  // 256-row workgroups, and for 128-row ones without the causal mask, where
+  // they measured faster; causal 128-row launches measured slower.
+  constexpr bool PRIO = MODE == 0 || (MODE == 1 && !CAUSAL);
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
@@ -500,6 +504,13 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, T::NFRAG>([&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
+      // Issue priority falls 3, 2, 1, 0 over the four quarters of the
+      // products.  The two waves of a SIMD run the same sequence; with equal
+      // priorities the older one wins every contested matrix-core slot and
+      // runs ahead while the younger one finishes the iteration alone.  A
+      // wave that is a quarter ahead now yields to the one behind.
+      if constexpr (PRIO && (8 * i) % (2 * T::NFRAG) == 0)
+        __builtin_amdgcn_s_setprio(3 - (8 * i) / (2 * T::NFRAG));
       if constexpr (i + 2 < T::NFRAG) {
         ka[i + 2] = kread(kb, i + 2);
         if constexpr (!FIRST) va[i + 2] = vread(vb, i + 2);
