@@ -35,8 +35,9 @@ the median per-call time gives TFLOP/s, the fraction of the matrix-core (or,
 for fp32, vector) peak, and algorithmic HBM GB/s against 8 TB/s.  The fp64
 oracle is timed beside each on the host: all cores, and one core for the
 small shapes; the long-context oracle computes 256 sampled rows per head and
-says so.  The shader clock is measured with a spin kernel that counts clock
-cycles, alone and while the headline step runs.
+says so.  The shader clock is measured by a one-wave probe kernel
+(libfa_clock.so) that reads the shader cycle counter against the 100 MHz
+real-time counter, alone and beside each of the step's main kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 """
@@ -478,39 +479,58 @@ def bench_workloads(with_cpu):
     return out
 
 
-def measure_clock(step):
-    """Shader clock from a one-wave spin kernel that waits a fixed number of
-    clock cycles (torch.cuda._sleep), timed with HIP events: alone, and on a
-    second stream while ``step`` runs on the current one (then the spin wave
-    shares the chip with the attention kernels and sees their clock)."""
-    cycles = 40_000_000
-    cur = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    torch.cuda._sleep(cycles)
-    e1.record()
-    torch.cuda.synchronize()
-    idle_ghz = cycles / (e0.elapsed_time(e1) * 1e-3) / 1e9
+def measure_clock(kernels):
+    """Shader clock from the probe library (libfa_clock.so): one wave spins
+    for N shader-clock cycles and reads the shader cycle counter and the
+    100 MHz real-time counter at its start and end.  Measured alone, and on a
+    second stream while each of ``kernels`` (name -> call) runs back to back
+    from a captured graph on the current stream (the spin wave then shares
+    the chip with that kernel and sees its clock)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_13_amd", "libfa_clock.so"))
+    lib.fa_clock_spin.restype = ctypes.c_int
+    lib.fa_clock_spin.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    buf = torch.zeros(4, dtype=torch.int64, device=dev)
     side = torch.cuda.Stream()
-    side.wait_stream(cur)
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # The spin (~10 ms) starts while the first steps run; the steps queued
-    # after it keep the chip busy for ~2.5x its length.
-    for _ in range(4):
-        step()
-    with torch.cuda.stream(side):
-        f0.record()
-        torch.cuda._sleep(cycles // 2)
-        f1.record()
-    for _ in range(40):
-        step()
-    torch.cuda.synchronize()
-    load_ghz = (cycles // 2) / (f0.elapsed_time(f1) * 1e-3) / 1e9
-    return {"idle_ghz": round(idle_ghz, 3), "under_load_ghz": round(load_ghz, 3),
-            "method": "spin kernel of N shader-clock cycles (torch.cuda._sleep) timed with HIP "
-                      "events; under load it runs on a second stream beside the headline step",
-            "published_peak_clock_ghz": 2.4}
+
+    def spin(cycles):
+        with torch.cuda.stream(side):
+            if lib.fa_clock_spin(buf.data_ptr(), cycles, side.cuda_stream) != 0:
+                raise RuntimeError("clock probe launch failed")
+
+    def ghz():
+        torch.cuda.synchronize()
+        t0, r0, t1, r1 = buf.tolist()
+        return (t1 - t0) / ((r1 - r0) / 100e6) / 1e9
+
+    spin(20_000_000)
+    out = {"idle_ghz": round(ghz(), 3)}
+    for name, call in kernels.items():
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            call()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(40):
+                call()
+        torch.cuda.synchronize()
+        vals = []
+        for _ in range(3):
+            g.replay()                 # the chip is busy before the spin starts
+            spin(8_000_000)
+            for _ in range(3):
+                g.replay()
+            vals.append(ghz())
+        out[name + "_ghz"] = round(sorted(vals)[1], 3)
+        del g
+    out["method"] = ("in-kernel shader cycle counter against the 100 MHz real-time counter, "
+                     "one spinning wave on a second stream; median of 3 per kernel")
+    out["published_peak_clock_ghz"] = 2.4
+    return out
 
 
 def main():
@@ -602,7 +622,12 @@ def main():
         b1.record()
         torch.cuda.synchronize()
         blocks.append(b0.elapsed_time(b1) / args.steps)
-    clock = measure_clock(step)
+    clock = measure_clock({
+        "fwd_bf16_kernel": lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=lse),
+        "bwd_dkdv_kernel": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, scale=w.scale, causal=True,
+                                                  dk=dk, dv=dv),
+        "bwd_dq_kernel": lambda: fa.fa_bwd_dq(q, k, v, do, ws, scale=w.scale, causal=True, dq=dq),
+    })
 
     f_fwd, f_bwd = flops(B, H, L, L, d, True)
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12

@@ -1,7 +1,9 @@
 """Builds libfa.so (the C-ABI attention library) for gfx950 with hipcc.
 
 Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
-parallel), then linked into ``libfa.so`` next to this file.  hipcc
+parallel), then linked into ``libfa.so`` next to this file.  The benchmark's
+shader-clock probe (``clock/clock_probe.hip``) is built apart, into
+``libfa_clock.so``: it is no part of the attention library.  hipcc
 cross-compiles for gfx950 without a GPU present.
 
 Run:  python -m exact_io_aware_13_amd.build
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+CLOCK_SRC = os.path.join(PKG, "clock", "clock_probe.hip")
+CLOCK_LIB = os.path.join(PKG, "libfa_clock.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU ops.
@@ -79,7 +83,21 @@ def build(verbose=False):
         if missing:
             raise RuntimeError("libfa links with undefined internal symbols: " + ", ".join(missing))
     os.replace(tmp, LIB)
+    build_clock_probe(cc)
     return LIB
+
+
+def build_clock_probe(cc=None):
+    """Compile the benchmark's shader-clock probe into libfa_clock.so."""
+    cc = cc or hipcc()
+    tmp = CLOCK_LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-O3", "-fPIC", "-shared", "-fvisibility=hidden",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", CLOCK_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, CLOCK_LIB)
+    return CLOCK_LIB
 
 
 if __name__ == "__main__":

@@ -38,9 +38,9 @@ fa_status check_shape(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64
   // Row counts bound the grids of the row-wise helper kernels.
   if (bh * Lq > (int64_t(1) << 34) || bh * Lk > (int64_t(1) << 34)) return FA_ERR_SHAPE;
   const int64_t rows_per_block =
-      in_dtype == FA_BF16 ? fa::kFwdBf16RowsPerBlock : fa::kF32RowsPerBlock;
-  // Grid sizes (x dimension) of the largest launch must fit.
-  if (bh * cdiv(Lq, rows_per_block) > INT32_MAX || bh * cdiv(Lk, fa::kF32RowsPerBlock) > INT32_MAX)
+      in_dtype == FA_BF16 ? fa::kBf16MinRowsPerBlock : fa::kF32RowsPerBlock;
+  // Grid sizes (x dimension) of the largest launch, query- or key-side, must fit.
+  if (bh * cdiv(Lq, rows_per_block) > INT32_MAX || bh * cdiv(Lk, rows_per_block) > INT32_MAX)
     return FA_ERR_SHAPE;
   return FA_OK;
 }

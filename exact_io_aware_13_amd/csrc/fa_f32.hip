@@ -2,15 +2,25 @@
 //
 // The fp32 path serves fp32 callers and small problems where the answer
 // must match the definition to ~1e-6 relative; it uses plain fp32 FMA, not
-// matrix cores.  Each thread owns one row; tiles of the other operand are
-// staged in LDS and read as broadcasts.  The forward uses the same online
-// softmax as the bf16 kernels (running max, running sum, rescaled
-// unnormalised accumulator; "How Flash Attention Improves Transformer Memory
-// Efficiency ...", section "The Three Running Statistics").  The backward
-// recomputes P from the saved lse (section "Backward Pass Efficiency") and
-// is split so that no atomics are needed: one kernel owns key rows (dK, dV),
-// one owns query rows (dQ).  Per-thread accumulators that would not fit in
-// registers live in thread-private LDS columns.
+// matrix cores.  The forward uses the same online softmax as the bf16
+// kernels (running max, running sum, rescaled unnormalised accumulator; "How
+// Flash Attention Improves Transformer Memory Efficiency ...", section "The
+// Three Running Statistics"); the backward recomputes P from the saved lse
+// (section "Backward Pass Efficiency") and is split so that no atomics are
+// needed: one kernel owns key rows (dK, dV), one owns query rows (dQ).
+//
+// Layout.  A row of the stationary operand (a query row in the forward and
+// the dQ kernel, a key row in the dK/dV kernel) is spread over LPR = D/16
+// consecutive lanes, each holding 16 of its columns in registers, so a
+// wave covers 64/LPR rows and no per-thread array grows with D.  A dot
+// product is 16 FMAs per lane and a reduction over the LPR lanes.  The four
+// waves of a workgroup share the same rows and split the streamed range
+// (keys, or queries for dK/dV) into four contiguous parts; each wave keeps
+// its own running statistics or partial sums, and the parts are combined in
+// LDS in a fixed order (the softmax merge of the running statistics for the
+// forward, plain sums for the gradients), so results are bitwise
+// reproducible.  Short sequences thus run on four times as many waves, which
+// is what bounds the latency of the smallest workloads.
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -18,81 +28,151 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = kF32RowsPerBlock;  // rows (threads) per workgroup
-constexpr int kTile = 32;                // rows of the streamed operand per LDS tile
+constexpr int kWaves = 4;        // waves per workgroup (they split the streamed range)
+constexpr int kCols = 16;        // columns of a row per lane
+constexpr int kGroup = 4;        // streamed rows per inner step
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void fwd_f32_kernel(const float* __restrict__ Q,
-                                                        const float* __restrict__ K,
-                                                        const float* __restrict__ V,
-                                                        float* __restrict__ O,
-                                                        float* __restrict__ LSE, int BH, int Lq,
-                                                        int Lk, int n_qt, float scale_log2) {
-  __shared__ float Kl[kTile][D];
-  __shared__ float Vl[kTile][D];
-  const int tid = wi_id();
-  const int bh = wg_id() % BH;
-  const int qt = wg_id() / BH;
-  const int qi = qt * kRows + tid;
-  const bool valid = qi < Lq;
-  const float* q = Q + ((size_t)bh * Lq + (valid ? qi : 0)) * D;
-  const float* Kb = K + (size_t)bh * Lk * D;
-  const float* Vb = V + (size_t)bh * Lk * D;
+template <int D>
+struct F32Tile {
+  static constexpr int LPR = D / kCols;        // lanes per row
+  static constexpr int RPW = 64 / LPR;         // rows per wave (= per workgroup)
+  static_assert(kCols * LPR == D, "head dimension split");
+};
 
-  float qr[D], acc[D];
+// Sum over the LPR consecutive lanes that hold one row.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qr[c] = q[c];
-    acc[c] = 0.f;
+  for (int o = 1; o < LPR; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ void load_cols(const float* p, float (&v)[kCols]) {
+  const f32x4* q = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < kCols / 4; ++i) {
+    const f32x4 x = q[i];
+    v[4 * i] = x[0];
+    v[4 * i + 1] = x[1];
+    v[4 * i + 2] = x[2];
+    v[4 * i + 3] = x[3];
   }
+}
+
+__device__ __forceinline__ void store_cols(float* p, const float (&v)[kCols], float s) {
+  f32x4* q = reinterpret_cast<f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < kCols / 4; ++i) {
+    f32x4 x;
+    x[0] = v[4 * i] * s;
+    x[1] = v[4 * i + 1] * s;
+    x[2] = v[4 * i + 2] * s;
+    x[3] = v[4 * i + 3] * s;
+    q[i] = x;
+  }
+}
+
+// The contiguous part [lo, hi) of [0, n) that wave w of kWaves takes.
+__device__ __forceinline__ void wave_part(int n, int w, int& lo, int& hi) {
+  const int chunk = (n + kWaves - 1) / kWaves;
+  lo = min(n, w * chunk);
+  hi = min(n, lo + chunk);
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int BH, int Lq, int Lk, float c) {
+  using T = F32Tile<D>;
+  __shared__ float sm[kWaves][T::RPW], sl[kWaves][T::RPW];
+  __shared__ float sacc[kWaves][64][kCols + 1];
+  const int tid = wi_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
+  const int bh = wg_id() % BH;
+  const int r0 = (wg_id() / BH) * T::RPW;
+  const int qi = r0 + r;
+  const bool valid = qi < Lq;
+  const size_t qrow = (size_t)bh * Lq + (valid ? qi : 0);
+  const float* Kb = K + (size_t)bh * Lk * D + cc * kCols;
+  const float* Vb = V + (size_t)bh * Lk * D + cc * kCols;
+
+  float q[kCols], acc[kCols];
+  load_cols(Q + qrow * D + cc * kCols, q);
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+  // Keys any row of the workgroup sees, split over the waves.
+  const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
+  int k_lo, k_hi;
+  wave_part(kend, w, k_lo, k_hi);
   float m = -INFINITY, l = 0.f;
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, qt * kRows + kRows);  // last key any row of this block sees, +1
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
-    __syncthreads();
-    for (int e = tid; e < kTile * D; e += kRows) {
-      const int r = e / D, c = e % D;
-      const bool in = k0 + r < Lk;
-      Kl[r][c] = in ? Kb[(size_t)(k0 + r) * D + c] : 0.f;
-      Vl[r][c] = in ? Vb[(size_t)(k0 + r) * D + c] : 0.f;
+  for (int j0 = k_lo; j0 < k_hi; j0 += kGroup) {
+    float kv[kGroup][kCols], vv[kGroup][kCols], t[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int j = min(j0 + g, k_hi - 1);  // past the part: a repeated, masked row
+      load_cols(Kb + (size_t)j * D, kv[g]);
+      load_cols(Vb + (size_t)j * D, vv[g]);
     }
-    __syncthreads();
-    float t[kTile];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int g = 0; g < kGroup; ++g) {
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(qr[c], Kl[j][c], dot);
-      const int kj = k0 + j;
-      t[j] = (kj < Lk && !(CAUSAL && kj > qi)) ? dot * scale_log2 : -INFINITY;
-      mx = fmaxf(mx, t[j]);
+      for (int i = 0; i < kCols; ++i) dot = fmaf(q[i], kv[g][i], dot);
+      dot = row_sum<T::LPR>(dot);
+      const int j = j0 + g;
+      t[g] = (j < k_hi && !(CAUSAL && j > qi)) ? dot * c : -INFINITY;
+      mx = fmaxf(mx, t[g]);
     }
     const float m_new = fmaxf(m, mx);
-    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+    // A row that has seen no visible key yet keeps m = -inf; its
+    // probabilities are exp2(-inf) = 0 against a reference of 0.
+    const float base = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m - base);
     m = m_new;
-    float rs = 0.f;
+    l *= alpha;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      t[j] = exp2f(t[j] - base);
-      rs += t[j];
-    }
-    l = alpha * l + rs;
+    for (int i = 0; i < kCols; ++i) acc[i] *= alpha;
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
-      float a = acc[c] * alpha;
+    for (int g = 0; g < kGroup; ++g) {
+      const float p = exp2f(t[g] - base);
+      l += p;
 #pragma unroll
-      for (int j = 0; j < kTile; ++j) a = fmaf(t[j], Vl[j][c], a);
-      acc[c] = a;
+      for (int i = 0; i < kCols; ++i) acc[i] = fmaf(p, vv[g][i], acc[i]);
     }
   }
-  if (valid) {
-    float* o = O + ((size_t)bh * Lq + qi) * D;
-    const float inv = 1.f / l;
+  // Merge the four parts: M = max_w m_w, l = sum_w l_w 2^(m_w - M),
+  // acc = sum_w acc_w 2^(m_w - M), in wave order.
+  if (cc == 0) {
+    sm[w][r] = m;
+    sl[w][r] = l;
+  }
 #pragma unroll
-    for (int c = 0; c < D; ++c) o[c] = acc[c] * inv;
-    LSE[(size_t)bh * Lq + qi] = (m + log2f(l)) * kLn2;
+  for (int i = 0; i < kCols; ++i) sacc[w][lane][i] = acc[i];
+  __syncthreads();
+  if (w == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm[ww][r]);
+    float lt = 0.f, o[kCols];
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = sm[ww][r];
+      const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      lt = fmaf(sl[ww][r], f, lt);
+#pragma unroll
+      for (int i = 0; i < kCols; ++i) o[i] = fmaf(sacc[ww][lane][i], f, o[i]);
+    }
+    if (valid) {
+      store_cols(O + qrow * D + cc * kCols, o, 1.f / lt);
+      if (cc == 0) LSE[qrow] = (M + log2f(lt)) * kLn2;
+    }
   }
 }
 
@@ -111,149 +191,185 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restric
   lse2[r] = lse[r] * kLog2e;
 }
 
-// dK and dV: one thread per key row j, looping over the queries that see it.
+// ---------------------------------------------------------------------------
+// dK and dV: a workgroup owns RPW key rows; its waves split the queries that
+// can see them, and the four partial sums are added in wave order.
+// ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dkdv_f32_kernel(
+__global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
-    float* __restrict__ dK, float* __restrict__ dV, int BH, int Lq, int Lk, float scale_log2,
+    float* __restrict__ dK, float* __restrict__ dV, int BH, int Lq, int Lk, float c,
     float scale) {
-  __shared__ float Ql[kTile][D];
-  __shared__ float Gl[kTile][D];
-  __shared__ float Ll[kTile], Dl[kTile];
-  __shared__ float accK[D][kRows];
-  __shared__ float accV[D][kRows];
+  using T = F32Tile<D>;
+  __shared__ float sk[kWaves][64][kCols + 1], sv[kWaves][64][kCols + 1];
   const int tid = wi_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
   const int bh = wg_id() % BH;
-  const int kblk = wg_id() / BH;
-  const int kj = kblk * kRows + tid;
+  const int k0 = (wg_id() / BH) * T::RPW;
+  const int kj = k0 + r;
   const bool valid = kj < Lk;
-  const float* kp = K + ((size_t)bh * Lk + (valid ? kj : 0)) * D;
-  const float* vp = V + ((size_t)bh * Lk + (valid ? kj : 0)) * D;
-  float kr[D], vr[D];
+  const size_t krow = (size_t)bh * Lk + (valid ? kj : 0);
+  float kr[kCols], vr[kCols], ak[kCols], av[kCols];
+  load_cols(K + krow * D + cc * kCols, kr);
+  load_cols(V + krow * D + cc * kCols, vr);
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    kr[c] = kp[c];
-    vr[c] = vp[c];
-    accK[c][tid] = 0.f;
-    accV[c][tid] = 0.f;
+  for (int i = 0; i < kCols; ++i) {
+    ak[i] = 0.f;
+    av[i] = 0.f;
   }
-  const float* Qb = Q + (size_t)bh * Lq * D;
-  const float* Gb = dO + (size_t)bh * Lq * D;
-  const int qstart = CAUSAL ? (kblk * kRows) / kTile * kTile : 0;
-  for (int q0 = qstart; q0 < Lq; q0 += kTile) {
-    __syncthreads();
-    for (int e = tid; e < kTile * D; e += kRows) {
-      const int r = e / D, c = e % D;
-      const bool in = q0 + r < Lq;
-      Ql[r][c] = in ? Qb[(size_t)(q0 + r) * D + c] : 0.f;
-      Gl[r][c] = in ? Gb[(size_t)(q0 + r) * D + c] : 0.f;
+  const float* Qb = Q + (size_t)bh * Lq * D + cc * kCols;
+  const float* Gb = dO + (size_t)bh * Lq * D + cc * kCols;
+  const float* Lb = LSE2 + (size_t)bh * Lq;
+  const float* Db = Dvec + (size_t)bh * Lq;
+  // Queries that can see a key of this workgroup, split over the waves.
+  const int qstart = CAUSAL ? min(Lq, k0) : 0;
+  int q_lo, q_hi;
+  wave_part(Lq - qstart, w, q_lo, q_hi);
+  q_lo += qstart;
+  q_hi += qstart;
+  for (int i0 = q_lo; i0 < q_hi; i0 += kGroup) {
+    float qv[kGroup][kCols], gv[kGroup][kCols], lv[kGroup], dv[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int i = min(i0 + g, q_hi - 1);
+      load_cols(Qb + (size_t)i * D, qv[g]);
+      load_cols(Gb + (size_t)i * D, gv[g]);
+      lv[g] = Lb[i];
+      dv[g] = Db[i];
     }
-    if (tid < kTile) {
-      const bool in = q0 + tid < Lq;
-      Ll[tid] = in ? LSE2[(size_t)bh * Lq + q0 + tid] : 0.f;
-      Dl[tid] = in ? Dvec[(size_t)bh * Lq + q0 + tid] : 0.f;
-    }
-    __syncthreads();
-    for (int i = 0; i < kTile; ++i) {
-      const int qi = q0 + i;
-      if (qi >= Lq) break;
-      if (CAUSAL && qi < kj) continue;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = fmaf(Ql[i][c], kr[c], s);
-        dp = fmaf(Gl[i][c], vr[c], dp);
+      for (int x = 0; x < kCols; ++x) {
+        s = fmaf(qv[g][x], kr[x], s);
+        dp = fmaf(gv[g][x], vr[x], dp);
       }
-      const float p = exp2f(s * scale_log2 - Ll[i]);
-      const float ds = p * (dp - Dl[i]);
+      s = row_sum<T::LPR>(s);
+      dp = row_sum<T::LPR>(dp);
+      const int i = i0 + g;
+      const bool vis = i < q_hi && !(CAUSAL && i < kj);
+      const float p = vis ? exp2f(s * c - lv[g]) : 0.f;
+      const float ds = p * (dp - dv[g]);
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        accV[c][tid] = fmaf(p, Gl[i][c], accV[c][tid]);
-        accK[c][tid] = fmaf(ds, Ql[i][c], accK[c][tid]);
+      for (int x = 0; x < kCols; ++x) {
+        av[x] = fmaf(p, gv[g][x], av[x]);
+        ak[x] = fmaf(ds, qv[g][x], ak[x]);
       }
     }
   }
-  if (valid) {
-    float* dk = dK + ((size_t)bh * Lk + kj) * D;
-    float* dv = dV + ((size_t)bh * Lk + kj) * D;
 #pragma unroll
-    for (int c = 0; c < D; ++c) {
-      dk[c] = scale * accK[c][tid];
-      dv[c] = accV[c][tid];
+  for (int x = 0; x < kCols; ++x) {
+    sk[w][lane][x] = ak[x];
+    sv[w][lane][x] = av[x];
+  }
+  __syncthreads();
+  if (w == 0 && valid) {
+    float tk[kCols], tv[kCols];
+#pragma unroll
+    for (int x = 0; x < kCols; ++x) {
+      tk[x] = sk[0][lane][x];
+      tv[x] = sv[0][lane][x];
     }
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww)
+#pragma unroll
+      for (int x = 0; x < kCols; ++x) {
+        tk[x] += sk[ww][lane][x];
+        tv[x] += sv[ww][lane][x];
+      }
+    store_cols(dK + krow * D + cc * kCols, tk, scale);
+    store_cols(dV + krow * D + cc * kCols, tv, 1.f);
   }
 }
 
-// dQ: one thread per query row i, looping over the keys it sees.
+// ---------------------------------------------------------------------------
+// dQ: a workgroup owns RPW query rows; its waves split the keys they see, and
+// the four partial sums are added in wave order.
+// ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kRows) void bwd_dq_f32_kernel(
+__global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
-    float* __restrict__ dQ, int BH, int Lq, int Lk, float scale_log2, float scale) {
-  __shared__ float Kl[kTile][D];
-  __shared__ float Vl[kTile][D];
-  __shared__ float accQ[D][kRows];
+    float* __restrict__ dQ, int BH, int Lq, int Lk, float c, float scale) {
+  using T = F32Tile<D>;
+  __shared__ float sq[kWaves][64][kCols + 1];
   const int tid = wi_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
   const int bh = wg_id() % BH;
-  const int qt = wg_id() / BH;
-  const int qi = qt * kRows + tid;
+  const int r0 = (wg_id() / BH) * T::RPW;
+  const int qi = r0 + r;
   const bool valid = qi < Lq;
-  const size_t row = (size_t)bh * Lq + (valid ? qi : 0);
-  float qr[D], gr[D];
+  const size_t qrow = (size_t)bh * Lq + (valid ? qi : 0);
+  float qr[kCols], gr[kCols], aq[kCols];
+  load_cols(Q + qrow * D + cc * kCols, qr);
+  load_cols(dO + qrow * D + cc * kCols, gr);
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qr[c] = Q[row * D + c];
-    gr[c] = dO[row * D + c];
-    accQ[c][tid] = 0.f;
-  }
-  const float lse2 = LSE2[row];
-  const float Di = Dvec[row];
-  const float* Kb = K + (size_t)bh * Lk * D;
-  const float* Vb = V + (size_t)bh * Lk * D;
-  int kend = Lk;
-  if (CAUSAL) kend = min(Lk, qt * kRows + kRows);
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
-    __syncthreads();
-    for (int e = tid; e < kTile * D; e += kRows) {
-      const int r = e / D, c = e % D;
-      const bool in = k0 + r < Lk;
-      Kl[r][c] = in ? Kb[(size_t)(k0 + r) * D + c] : 0.f;
-      Vl[r][c] = in ? Vb[(size_t)(k0 + r) * D + c] : 0.f;
+  for (int i = 0; i < kCols; ++i) aq[i] = 0.f;
+  const float lse2 = LSE2[qrow];
+  const float Di = Dvec[qrow];
+  const float* Kb = K + (size_t)bh * Lk * D + cc * kCols;
+  const float* Vb = V + (size_t)bh * Lk * D + cc * kCols;
+  const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
+  int k_lo, k_hi;
+  wave_part(kend, w, k_lo, k_hi);
+  for (int j0 = k_lo; j0 < k_hi; j0 += kGroup) {
+    float kv[kGroup][kCols], vv[kGroup][kCols];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int j = min(j0 + g, k_hi - 1);
+      load_cols(Kb + (size_t)j * D, kv[g]);
+      load_cols(Vb + (size_t)j * D, vv[g]);
     }
-    __syncthreads();
-    for (int j = 0; j < kTile; ++j) {
-      const int kj = k0 + j;
-      if (kj >= Lk || (CAUSAL && kj > qi)) break;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        s = fmaf(qr[c], Kl[j][c], s);
-        dp = fmaf(gr[c], Vl[j][c], dp);
+      for (int x = 0; x < kCols; ++x) {
+        s = fmaf(qr[x], kv[g][x], s);
+        dp = fmaf(gr[x], vv[g][x], dp);
       }
-      const float ds = exp2f(s * scale_log2 - lse2) * (dp - Di);
+      s = row_sum<T::LPR>(s);
+      dp = row_sum<T::LPR>(dp);
+      const int j = j0 + g;
+      const bool vis = j < k_hi && !(CAUSAL && j > qi);
+      const float ds = vis ? exp2f(s * c - lse2) * (dp - Di) : 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) accQ[c][tid] = fmaf(ds, Kl[j][c], accQ[c][tid]);
+      for (int x = 0; x < kCols; ++x) aq[x] = fmaf(ds, kv[g][x], aq[x]);
     }
   }
-  if (valid) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) dQ[row * D + c] = scale * accQ[c][tid];
+  for (int x = 0; x < kCols; ++x) sq[w][lane][x] = aq[x];
+  __syncthreads();
+  if (w == 0 && valid) {
+    float t[kCols];
+#pragma unroll
+    for (int x = 0; x < kCols; ++x) t[x] = sq[0][lane][x];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww)
+#pragma unroll
+      for (int x = 0; x < kCols; ++x) t[x] += sq[ww][lane][x];
+    store_cols(dQ + qrow * D + cc * kCols, t, scale);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream) {
-  const int n_qt = (a.Lq + kRows - 1) / kRows;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(kRows), 0,
-                     stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+  using T = F32Tile<D>;
+  const int n_qt = (a.Lq + T::RPW - 1) / T::RPW;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(64 * kWaves),
+                     0, stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
                      static_cast<const float*>(a.V), static_cast<float*>(a.O), a.lse, a.BH, a.Lq,
-                     a.Lk, n_qt, a.scale * kLog2e);
+                     a.Lk, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t bwd_launch(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+  using T = F32Tile<D>;
   const int64_t rows = (int64_t)a.BH * a.Lq;
   const auto* Q = static_cast<const float*>(a.Q);
   const auto* K = static_cast<const float*>(a.K);
@@ -262,16 +378,17 @@ hipError_t bwd_launch(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   if ((stages & kBwdPrepare) && rows > 0)
     hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                        stream, static_cast<const float*>(a.O), G, a.lse, a.Dvec, a.lse2, rows);
-  const int n_kt = (a.Lk + kRows - 1) / kRows;
+  const int n_kt = (a.Lk + T::RPW - 1) / T::RPW;
   if ((stages & kBwdDkDv) && n_kt > 0)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)), dim3(kRows),
-                       0, stream, Q, K, V, G, a.lse2, a.Dvec, static_cast<float*>(a.dK),
-                       static_cast<float*>(a.dV), a.BH, a.Lq, a.Lk, a.scale * kLog2e, a.scale);
-  const int n_qt = (a.Lq + kRows - 1) / kRows;
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)),
+                       dim3(64 * kWaves), 0, stream, Q, K, V, G, a.lse2, a.Dvec,
+                       static_cast<float*>(a.dK), static_cast<float*>(a.dV), a.BH, a.Lq, a.Lk,
+                       a.scale * kLog2e, a.scale);
+  const int n_qt = (a.Lq + T::RPW - 1) / T::RPW;
   if ((stages & kBwdDq) && n_qt > 0)
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(kRows),
-                       0, stream, Q, K, V, G, a.lse2, a.Dvec, static_cast<float*>(a.dQ), a.BH,
-                       a.Lq, a.Lk, a.scale * kLog2e, a.scale);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)),
+                       dim3(64 * kWaves), 0, stream, Q, K, V, G, a.lse2, a.Dvec,
+                       static_cast<float*>(a.dQ), a.BH, a.Lq, a.Lk, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

@@ -86,7 +86,8 @@ hipError_t launch_splitkv_bf16(const SplitKvArgs& a, unsigned stages, hipStream_
 
 // Work decomposition shared by validation and the launchers.
 constexpr int kFwdBf16RowsPerBlock = 256;
+constexpr int kBf16MinRowsPerBlock = 128;  // fewest query or key rows of any bf16 workgroup
 constexpr int kBwdBf16KeysPerBlock = 128;
-constexpr int kF32RowsPerBlock = 64;
+constexpr int kF32RowsPerBlock = 8;        // fewest rows of an fp32 workgroup (d = 128)
 
 }  // namespace fa

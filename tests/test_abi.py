@@ -271,3 +271,4 @@ def test_bwd_blocksparse_rejects(lib):
     assert call(mask=None) == NULL
     assert call(ws=8) == WS
     assert call(Lk=4096 * 128 + 1) == UNSUP
+
