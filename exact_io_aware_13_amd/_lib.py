@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
-           "fa_fwd_splitkv_default_splits", "fa_status_str", "fa_version")
+           "fa_fwd_splitkv_default_splits", "fa_bwd_noalloc", "fa_bwd_noalloc_max_scratch_bytes",
+           "fa_status_str", "fa_version")
 
 _lib = None
 
@@ -75,6 +76,11 @@ def _declare(lib):
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
     lib.fa_fwd_splitkv_default_splits.restype = i64
     lib.fa_fwd_splitkv_default_splits.argtypes = [i64, i64, i64, i64, i64]
+    lib.fa_bwd_noalloc.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, f32,
+                                   i32, vp, vp, vp, vp]
+    lib.fa_bwd_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_noalloc_max_scratch_bytes.argtypes = []
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [i32]
     lib.fa_version.restype = ctypes.c_char_p

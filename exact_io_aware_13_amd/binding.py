@@ -170,6 +170,35 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
     return dq, dk, dv
 
 
+def fa_bwd_noalloc_max_scratch_bytes():
+    """Bytes of the fixed statistics array ``fa_bwd_noalloc`` uses per GPU."""
+    return int(_lib.load().fa_bwd_noalloc_max_scratch_bytes())
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False):
+    """dQ, dK, dV through libfa's ``fa_bwd_noalloc``: ``fa_bwd`` with its
+    statistics in the library's fixed per-GPU array instead of a workspace.
+    The outputs must be given (nothing is allocated, here or in the call);
+    calls that overlap on one GPU race on that array."""
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dev = q.device
+    _check_tensor("q", q, dev)
+    for name, t, shp in (("k", k, (B, H, Lk, d)), ("v", v, (B, H, Lk, d)),
+                         ("do", do, (B, H, Lq, d)), ("dq", dq, (B, H, Lq, d)),
+                         ("dk", dk, (B, H, Lk, d)), ("dv", dv, (B, H, Lk, d))):
+        _check_tensor(name, t, dev, q.dtype, shp)
+    _check_tensor("o", o, dev, None, (B, H, Lq, d))
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib.load().fa_bwd_noalloc(_code(q.dtype), _code(o.dtype), B, H, Lq, Lk, d, _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), float(scale),
+                                    int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _stream(dev))
+    _lib.check(st)
+    return dq, dk, dv
+
+
 def fa_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=False, dq=None,
                        dk=None, dv=None, workspace=None):
     """dQ, dK, dV through libfa's ``fa_bwd_blocksparse``: the backward of

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -385,6 +386,78 @@ fa_status fa_bwd_blocksparse(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int
   return bwd_stages(fa::kBwdAll, in_dtype, o_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale,
                     causal, dQ, dK, dV, workspace, workspace_bytes, stream, block_mask,
                     mask_slices);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward without a caller-provided workspace: the per-row statistics live
+// in a fixed device array of this library instead.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;  // D and base-2 lse for up to 2^21 rows
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU the library runs on, held until the process ends.  Host
+// code never passes the name itself to a kernel or a copy: on the host it
+// names a stand-in, not device memory.  The device address comes from
+// hipGetSymbolAddress, once per device (scratch_address).
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the NULL stream); looked up the first time with that device
+// current, then reused.
+fa_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return FA_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+fa_status fa_bwd_noalloc(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H, int64_t Lq,
+                         int64_t Lk, int64_t d, const void* Q, const void* K, const void* V,
+                         const void* O, const void* dO, const float* lse, float scale, int causal,
+                         void* dQ, void* dK, void* dV, hipStream_t stream) {
+  // The same checks as fa_bwd, in the same order, before the scratch
+  // address is looked up: a call they reject makes no HIP call.
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !std::isfinite(scale)) return FA_ERR_ARG;
+  if (fa_status st = check_shape(in_dtype, B, H, Lq, Lk, d)) return st;
+  if (in_dtype == FA_F32 && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (fa_bwd_workspace_bytes(in_dtype, B, H, Lq, Lk, d) > kScratchBytes) return FA_ERR_WORKSPACE;
+  const bool has_q = B * H * Lq > 0, has_k = B * H * Lk > 0;
+  if (!has_q && !has_k) return FA_OK;
+  if (has_q && (!Q || !K || !V || !O || !dO || !lse || !dQ)) return FA_ERR_NULL;
+  if (has_k && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  if (fa_status st = scratch_address(stream, &ws)) return st;
+  return bwd_stages(fa::kBwdAll, in_dtype, o_dtype, B, H, Lq, Lk, d, Q, K, V, O, dO, lse, scale,
+                    causal, dQ, dK, dV, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

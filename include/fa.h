@@ -311,6 +311,32 @@ FA_API fa_status fa_bwd_blocksparse(fa_dtype in_dtype, fa_dtype o_dtype,
                  void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): fa_bwd
+ * with no workspace argument.  The per-row statistics (D and base-2 lse)
+ * go to a fixed array inside the library, one per GPU, of
+ * fa_bwd_noalloc_max_scratch_bytes() bytes (16 MiB: up to 2^21 query rows,
+ * B*H*Lq); each GPU holds its copy until the process ends.  Sizes whose
+ * statistics need more return FA_ERR_WORKSPACE before any HIP call.  The
+ * call allocates and frees nothing.
+ *
+ * Every call on one GPU uses that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different threads) race and must be
+ * ordered by the caller.  The array keeps the previous call's contents;
+ * nothing in it needs to start at zero.  The first call on a device looks
+ * up the array's device address (with that device current), which needs no
+ * allocation.  Other arguments, checks, outputs and status codes as for
+ * fa_bwd; the results are bitwise those of fa_bwd.
+ */
+FA_API size_t fa_bwd_noalloc_max_scratch_bytes(void);
+FA_API fa_status fa_bwd_noalloc(fa_dtype in_dtype, fa_dtype o_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse,
+                 float scale, int causal,
+                 void* dQ, void* dK, void* dV, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 FA_API const char* fa_status_str(fa_status s);
 

@@ -272,3 +272,40 @@ def test_bwd_blocksparse_rejects(lib):
     assert call(ws=8) == WS
     assert call(Lk=4096 * 128 + 1) == UNSUP
 
+
+# ---- backward without a workspace argument --------------------------------
+
+def _bwd_na(lib, in_dt=BF16, o_dt=None, B=1, H=2, Lq=64, Lk=64, d=128, ptrs=None, scale=0.125,
+            causal=1):
+    p = dict(Q=P, K=P, V=P, O=P, dO=P, lse=P, dQ=P, dK=P, dV=P)
+    p.update(ptrs or {})
+    o_dt = in_dt if o_dt is None else o_dt
+    return lib.fa_bwd_noalloc(in_dt, o_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["O"],
+                              p["dO"], p["lse"], scale, causal, p["dQ"], p["dK"], p["dV"], None)
+
+
+def test_noalloc_scratch_size(lib):
+    # 16 MiB: D and the base-2 lse (4 bytes each) for 2^21 query rows.
+    assert lib.fa_bwd_noalloc_max_scratch_bytes() == 16 * 2 ** 20
+    rows = 2 ** 21
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 1, rows, 64, 64) == 16 * 2 ** 20
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_dt=9), ARG), (dict(o_dt=5), ARG), (dict(scale=float("nan")), ARG),
+    (dict(in_dt=F32, o_dt=BF16), UNSUP), (dict(d=96), UNSUP), (dict(Lk=0), SHAPE),
+    (dict(B=1 << 40, H=1 << 40), SHAPE),
+    # Statistics beyond the fixed array: one row more than 2^21, in any split.
+    (dict(B=1, H=1, Lq=2 ** 21 + 1, Lk=64, d=64), WS), (dict(B=4, H=8, Lq=65537, d=64), WS),
+    (dict(ptrs=dict(dQ=None)), NULL), (dict(ptrs=dict(lse=None)), NULL),
+    (dict(ptrs=dict(K=None)), NULL), (dict(ptrs=dict(dV=P + 8)), ALIGN),
+    (dict(ptrs=dict(O=P + 4)), ALIGN),
+])
+def test_noalloc_rejects_before_any_hip_call(lib, kw, status):
+    assert _bwd_na(lib, **kw) == status
+
+
+def test_noalloc_empty_is_ok(lib):
+    nul = {k: None for k in ("Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV")}
+    assert _bwd_na(lib, B=0, ptrs=nul) == OK
+    assert _bwd_na(lib, Lq=0, Lk=0, ptrs=nul) == OK
