@@ -185,11 +185,7 @@ def _reference_move_inputs(kind, Lq, Lk, d, seed):
         kf[:, :, Lk - 5, 0] = 2000.0
     elif kind == "spread":    # large score spread everywhere
         qf, kf = qf * 3.0, kf * 3.0
-    # Peaked rows put most weight on a few keys, each probability rounded to
-    # bf16 for the value product; the output error of that rounding scales
-    # with |V|, so V is halved to stay inside the bf16 bound (the reference
-    # moves depend on Q and K only).
-    return qf.to(torch.bfloat16), kf.to(torch.bfloat16), (0.5 * v.float()).to(torch.bfloat16)
+    return qf.to(torch.bfloat16), kf.to(torch.bfloat16), v
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -204,4 +200,17 @@ def test_reference_moves_late(kind, causal, d):
     torch.cuda.synchronize()
     O_ref, lse_ref = oracle.attn_fwd(f64(q), f64(k), f64(v), scale, causal)
     assert np.isfinite(f64(O)).all() and np.isfinite(f64(lse)).all()
-    assert_bf16_fwd(fwd_errors(f64(O), f64(lse), O_ref, lse_ref), f"{kind} d{d} causal={causal}")
+    # Peaked rows put nearly all weight on a few keys, so the bf16 rounding
+    # of those probabilities (for the value product) and of the output is
+    # not averaged away.  Each rounds to nearest with unit roundoff
+    # u = 2^-8, so per element |dO_ic| <= 2u sum_j P_ij |V_jc|: the oracle's
+    # output with |V| as the values bounds the error, elementwise and hence
+    # in the mean (the 1e-2 / 1e-3 bars hold for spread-out rows of N(0,1)
+    # values).  lse does not depend on V.
+    e = fwd_errors(f64(O), f64(lse), O_ref, lse_ref)
+    O_abs, _ = oracle.attn_fwd(f64(q), f64(k), np.abs(f64(v)), scale, causal)
+    u = 2.0 ** -8
+    what = f"{kind} d{d} causal={causal}"
+    assert e["o_max"] <= 2 * u * O_abs.max(), f"{what}: {e}"
+    assert e["o_mean"] <= 2 * u * O_abs.mean(), f"{what}: {e}"
+    assert e["lse_max"] <= 1e-3, f"{what}: {e}"
