@@ -549,11 +549,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dQ kernel
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool HALF>
 struct DqTile {
   // 8 waves of one 32-row block (two waves per SIMD, each within 256
-  // registers).
-  static constexpr int NW = 8;                    // waves per workgroup
+  // registers).  HALF (the block-sparse backward): 4 waves, 128 rows -- one
+  // row block of the mask -- and two workgroups per compute unit.
+  static constexpr int NW = HALF ? 4 : 8;         // waves per workgroup
   static constexpr int RB = 1;                    // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
   static constexpr int BC = D == 128 ? 32 : 64;   // keys per tile
@@ -574,18 +575,17 @@ struct DqTile {
   static_assert(LOADS >= 1, "tile split");
 };
 
-// SPARSE: block-sparse backward -- the workgroup's 256 rows are two row
-// blocks of the mask; it visits the key blocks either of them sees (a
-// compacted list with one flag per row block), and a wave whose row block
-// does not see a listed block zeroes that tile's probabilities.
+// SPARSE: block-sparse backward -- the workgroup's 128 rows are one row
+// block of the mask, and it visits the key blocks that row block sees (a
+// compacted list read through register windows, as in the forward).
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__((64 * DqTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
     int BH, int Lq, int Lk, int n_qt, float c, float scale,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
-  using T = DqTile<D>;
+  using T = DqTile<D, SPARSE>;
   // 4-slot rings for K and V, one LDS array per slot.
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
@@ -632,27 +632,25 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
   int nkt = (Lk + T::BC - 1) / T::BC;
   if (CAUSAL) nkt = min(nkt, (q0 + T::BR - 1) / T::BC + 1);
 
-  // ---- block-sparse: key blocks either row block sees ------------------------
-  // Entry: key block in bits 0..13, bit 14 + b set if row block b sees it.
+  // ---- block-sparse: the key blocks this row block sees ----------------------
+  // Entry: key block in bits 0..13; bit 14 set (the workgroup's one row
+  // block sees it -- every listed block, kept in the format the tile masks
+  // read).
   constexpr int TPB = kSparseBlock / T::BC;  // key tiles per mask block
   __shared__ uint16_t klist[SPARSE ? kSparseMaxKeyBlocks : 1];
   __shared__ int wtot[SPARSE ? T::NW : 1];
-  const int wq = (32 * T::RB * w) / kSparseBlock;  // this wave's row block
+  const int wq = (32 * T::RB * w) / kSparseBlock;  // this wave's row block (0)
   int nlist = 0, wbase = 0;
   unsigned win0 = 0, win1 = 0;
   if constexpr (SPARSE) {
-    static_assert(T::BR == 2 * kSparseBlock, "two mask row blocks per workgroup");
+    static_assert(T::BR == kSparseBlock, "one mask row block per workgroup");
     const int qb0 = q0 / kSparseBlock;
-    const bool has1 = qb0 + 1 < nqb;
     const uint8_t* row0 = BM + (size_t)bh * bm_stride + (size_t)qb0 * nkb;
-    const uint8_t* row1 = row0 + nkb;
     const int kb_lim = CAUSAL ? min(nkb, (q0 + T::BR - 1) / kSparseBlock + 1) : nkb;
     for (int base = 0; base < kb_lim; base += 64 * T::NW) {
       const int kb = base + tid;
-      const bool in = kb < kb_lim;
-      const bool f0 = in && row0[kb] != 0;
-      const bool f1 = in && has1 && row1[kb] != 0;
-      const uint64_t bal = __ballot(f0 || f1);
+      const bool f0 = kb < kb_lim && row0[kb] != 0;
+      const uint64_t bal = __ballot(f0);
       const int below = __popcll(bal & ((uint64_t(1) << lane) - 1));
       if (lane == 0) wtot[w] = __popcll(bal);
       __syncthreads();
@@ -661,7 +659,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
         if (ww < w) off += wtot[ww];
         tot += wtot[ww];
       }
-      if (f0 || f1) klist[off + below] = (uint16_t)(kb | (int(f0) << 14) | (int(f1) << 15));
+      if (f0) klist[off + below] = (uint16_t)(kb | (1 << 14));
       nlist += tot;
       __syncthreads();
     }
@@ -1041,7 +1039,7 @@ __global__ __launch_bounds__(64 * DqTile<D>::NW, 1) void bwd_dq_kernel(
 template <int D, bool CAUSAL, bool SPARSE>
 void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   using TK = KvTile<D>;
-  using TQ = DqTile<D>;
+  using TQ = DqTile<D, SPARSE>;
   const float c = a.scale * kLog2e;
   const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
   const uint16_t* K = static_cast<const uint16_t*>(a.K);

@@ -298,8 +298,8 @@ FA_API fa_status fa_fwd_splitkv_merge(fa_dtype out_dtype,
  * o_dtype, workspace, layouts and status codes as for fa_bwd; supported: in_dtype
  * FA_BF16, d in {64, 128}, ceil(Lq/128) and ceil(Lk/128) <= 4096 (else
  * FA_ERR_UNSUPPORTED).  The key-side kernel visits only the query blocks
- * that see its key block; the query side visits the key blocks either of a
- * workgroup's two 128-row blocks sees.
+ * that see its key block; the query side only the key blocks its 128-row
+ * block (one row block of the mask) sees.
  */
 FA_API fa_status fa_bwd_blocksparse(fa_dtype in_dtype, fa_dtype o_dtype,
                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,

@@ -197,7 +197,12 @@ def test_backward_window_pattern_benchmark_size_two_heads():
     announce("blocksparse bwd window pattern B1 H32 L4096 d128 causal")
     O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=w.scale, causal=True)
     grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=w.scale, causal=True)
+    # A second call gives the same bits (every gradient row is summed in a
+    # fixed order by one workgroup).
+    again = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=w.scale, causal=True)
     torch.cuda.synchronize()
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b)
     for h in (0, 17):
         sl = lambda t: to_f64(t[:, h:h + 1])
         ref = oracle.attn_bwd_blocksparse(sl(q), sl(k), sl(v), sl(do), w.scale, True, bm.numpy(),
@@ -248,7 +253,11 @@ def test_long_query_block_list_backward():
     announce("blocksparse long query list")
     O, lse = fa.fa_fwd_blocksparse(qd, kd, vd, bmd, scale=scale)
     grads = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=scale)
+    again = fa.fa_bwd_blocksparse(qd, kd, vd, O, dod, lse, bmd, scale=scale)
     torch.cuda.synchronize()
+    # Lists of over 200 entries: the same bits again on a second call.
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b)
     for g, r, name in zip(grads, ref, ("dQ", "dK", "dV")):
         err = rel_to_max(to_f64(g), r)
         assert err <= BF16_GRAD_REL, f"long query list {name}: rel-to-max {err:.3e}"
