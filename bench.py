@@ -40,6 +40,7 @@ says so.  The shader clock is measured by a one-wave probe kernel
 real-time counter, alone and beside each of the step's main kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                       [--no-workloads]
 """
 
 import argparse
@@ -541,6 +542,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode and block-sparse forwards measured after the main step")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload measurements (other shapes; used when profiling "
+                         "the headline step's kernels by name)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -680,10 +684,11 @@ def main():
                     "median_tflops": round((f_fwd + f_bwd) / (sorted(blocks)[2] * 1e-3) / 1e12, 2)},
         "clock": clock,
     }
-    try:
-        line["workloads"] = bench_workloads(not args.no_cpu_baseline)
-    except Exception as e:  # noqa: BLE001  (recorded instead of losing the main line)
-        line["workloads"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_workloads:
+        try:
+            line["workloads"] = bench_workloads(not args.no_cpu_baseline)
+        except Exception as e:  # noqa: BLE001  (recorded instead of losing the main line)
+            line["workloads"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_decode:
         # Measured after the timed steps above; not part of value.  A failure
         # here is recorded in the line instead of losing the main measurement.
