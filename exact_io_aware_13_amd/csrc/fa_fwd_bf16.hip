@@ -171,7 +171,16 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   // causal masks the tiles with the most visible keys are dispatched first.
   const int bh = wg_id() % BH;
   int qt = wg_id() / BH;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  if (CAUSAL) {
+    // When every workgroup of a 128-row causal launch is resident at once
+    // (two per compute unit), workgroups g and g + grid/2 share a compute
+    // unit: the second half runs lightest-first so that each pair holds
+    // about the same number of key tiles.  Otherwise heaviest first.
+    if (MODE == 1 && (n_qt & 1) == 0 && n_qt * BH <= 2 * kComputeUnits && qt >= n_qt / 2)
+      qt -= n_qt / 2;
+    else
+      qt = n_qt - 1 - qt;
+  }
   const int q0 = qt * T::BR;
   const int qw0 = q0 + 32 * T::RB * w;  // this wave's first row
 
@@ -738,7 +747,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   // (gfx950: 256 compute units); then 128-row ones, which also halve the
   // longest workgroup's work under a causal mask.
   const int64_t wgs256 = (int64_t)((a.Lq + 255) / 256) * a.BH;
-  if (wgs256 < 512) return a.d == 64 ? launch_d<64, 1>(a, stream) : launch_d<128, 1>(a, stream);
+  if (wgs256 < 2 * kComputeUnits) return a.d == 64 ? launch_d<64, 1>(a, stream) : launch_d<128, 1>(a, stream);
   return a.d == 64 ? launch_d<64, 0>(a, stream) : launch_d<128, 0>(a, stream);
 }
 

@@ -85,6 +85,7 @@ hipError_t launch_bwd_f32(const BwdArgs& a, unsigned stages, hipStream_t stream)
 hipError_t launch_splitkv_bf16(const SplitKvArgs& a, unsigned stages, hipStream_t stream);
 
 // Work decomposition shared by validation and the launchers.
+constexpr int kComputeUnits = 256;  // MI355X (gfx950)
 constexpr int kFwdBf16RowsPerBlock = 256;
 constexpr int kBf16MinRowsPerBlock = 128;  // fewest query or key rows of any bf16 workgroup
 constexpr int kBwdBf16KeysPerBlock = 128;
