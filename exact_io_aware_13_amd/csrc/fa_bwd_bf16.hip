@@ -552,8 +552,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 template <int D, bool HALF>
 struct DqTile {
   // 8 waves of one 32-row block (two waves per SIMD, each within 256
-  // registers).  HALF (the block-sparse backward): 4 waves, 128 rows -- one
-  // row block of the mask -- and two workgroups per compute unit.
+  // registers).  HALF: 4 waves, 128 rows, two workgroups per compute unit --
+  // for launches that would otherwise give fewer than two workgroups per
+  // compute unit, and for the block-sparse backward (one mask row block per
+  // workgroup).
   static constexpr int NW = HALF ? 4 : 8;         // waves per workgroup
   static constexpr int RB = 1;                    // 32-row blocks per wave
   static constexpr int BR = 32 * RB * NW;         // query rows per workgroup
@@ -575,17 +577,19 @@ struct DqTile {
   static_assert(LOADS >= 1, "tile split");
 };
 
-// SPARSE: block-sparse backward -- the workgroup's 128 rows are one row
-// block of the mask, and it visits the key blocks that row block sees (a
-// compacted list read through register windows, as in the forward).
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__((64 * DqTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) void bwd_dq_kernel(
+// MODE: 0 dense, 256 rows per workgroup; 1 dense, 128 rows; 2 block-sparse,
+// 128 rows -- one row block of the mask, visiting the key blocks that row
+// block sees (a compacted list read through register windows, as in the
+// forward).
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__((64 * DqTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
     int BH, int Lq, int Lk, int n_qt, float c, float scale,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
-  using T = DqTile<D, SPARSE>;
+  using T = DqTile<D, MODE != 0>;
+  constexpr bool SPARSE = MODE == 2;
   // 4-slot rings for K and V, one LDS array per slot.
   __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
   __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
@@ -615,9 +619,17 @@ __global__ __launch_bounds__((64 * DqTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) voi
   const int lane = tid & 63, n = lane & 31, h = lane >> 5;
   // Same tile order as the forward: consecutive workgroups take the same
   // query tile of different slices, the most expensive causal tiles first.
+  // With 128-row causal tiles all resident at once, workgroups g and
+  // g + grid/2 share a compute unit, and the second half runs lightest-first
+  // (the forward's rule).
   const int bh = wg_id() % BH;
   int qt = wg_id() / BH;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  if (CAUSAL) {
+    if (MODE == 1 && (n_qt & 1) == 0 && n_qt * BH <= 2 * kComputeUnits && qt >= n_qt / 2)
+      qt -= n_qt / 2;
+    else
+      qt = n_qt - 1 - qt;
+  }
   const int q0 = qt * T::BR;
   const int qw0 = q0 + 32 * T::RB * w;
 
@@ -906,7 +918,8 @@ __global__ __launch_bounds__((64 * DqTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) voi
       // iteration's products, so the wave of a SIMD pair that runs ahead
       // yields contested matrix-core slots to the one behind (as in the
       // forward).
-      if constexpr ((4 * i) % NALL == 0) __builtin_amdgcn_s_setprio(3 - (4 * i) / NALL);
+      if constexpr (!(MODE == 1 && CAUSAL) && (4 * i) % NALL == 0)
+        __builtin_amdgcn_s_setprio(3 - (4 * i) / NALL);
       product(Ic);
       slot(Ic);
       __builtin_amdgcn_sched_barrier(0);
@@ -1036,10 +1049,11 @@ __global__ __launch_bounds__((64 * DqTile<D, SPARSE>::NW), (SPARSE ? 2 : 1)) voi
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, int QMODE>
 void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+  constexpr bool SPARSE = QMODE == 2;
   using TK = KvTile<D>;
-  using TQ = DqTile<D, SPARSE>;
+  using TQ = DqTile<D, QMODE != 0>;
   const float c = a.scale * kLog2e;
   const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
   const uint16_t* K = static_cast<const uint16_t*>(a.K);
@@ -1053,7 +1067,7 @@ void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
                        c, a.scale, a.block_mask, a.bm_stride, a.nqb, a.nkb);
   const int n_qt = (a.Lq + TQ::BR - 1) / TQ::BR;
   if ((stages & kBwdDq) && n_qt > 0 && a.Lk > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)(n_qt * a.BH)),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QMODE>), dim3((unsigned)(n_qt * a.BH)),
                        dim3(64 * TQ::NW), 0, stream, Q, K, V, dO, a.lse2, a.Dvec,
                        static_cast<uint16_t*>(a.dQ), a.BH, a.Lq, a.Lk, n_qt, c, a.scale,
                        a.block_mask, a.bm_stride, a.nqb, a.nkb);
@@ -1072,12 +1086,18 @@ hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a.O,
                          static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
   }
+  // dQ: 256-row workgroups unless that gives fewer than two per compute
+  // unit; then 128-row ones (as the forward).
+  const int64_t wgs256 = (int64_t)((a.Lq + 255) / 256) * a.BH;
   if (a.block_mask) {
-    if (a.causal) launch_main<D, true, true>(a, stages, stream);
-    else launch_main<D, false, true>(a, stages, stream);
+    if (a.causal) launch_main<D, true, 2>(a, stages, stream);
+    else launch_main<D, false, 2>(a, stages, stream);
+  } else if (wgs256 < 2 * kComputeUnits) {
+    if (a.causal) launch_main<D, true, 1>(a, stages, stream);
+    else launch_main<D, false, 1>(a, stages, stream);
   } else {
-    if (a.causal) launch_main<D, true, false>(a, stages, stream);
-    else launch_main<D, false, false>(a, stages, stream);
+    if (a.causal) launch_main<D, true, 0>(a, stages, stream);
+    else launch_main<D, false, 0>(a, stages, stream);
   }
   return hipGetLastError();
 }
