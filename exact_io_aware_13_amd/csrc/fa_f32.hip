@@ -24,6 +24,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_tile.h"
 
 namespace fa {
 namespace {
@@ -82,11 +83,44 @@ __device__ __forceinline__ void wave_part(int n, int w, int& lo, int& hi) {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
+// Each wave streams its key part through a private ring of kRing LDS slots,
+// filled by direct-to-LDS buffer loads kRing-1 chunks ahead of use: a wave
+// reads only what it loaded itself, so its own s_waitcnt suffices (no
+// barrier), and a short part costs one memory latency instead of one per
+// group of keys.
+constexpr int kRing = 4;
+
+template <int D>
+struct F32Ring {
+  static constexpr int CH = kGroup;          // keys per chunk
+  static constexpr int ROWB = D * 4;         // bytes per key row
+  static constexpr int RPI = 1024 / ROWB;    // rows per 1-KiB load instruction
+  static constexpr int LPC = CH / RPI;       // load instructions per tensor per chunk
+  static constexpr int CHB = CH * ROWB;      // bytes per chunk of one tensor
+  static constexpr int SLOTB = 2 * CHB;      // K then V
+  static_assert(LPC >= 1 && LPC * RPI == CH, "chunk split");
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Lq, int Lk, float c) {
   using T = F32Tile<D>;
+  using RG = F32Ring<D>;
+  // One array per ring slot (every wave's part of it), selected at compile
+  // time, so the compiler relates each LDS read only to its own slot's loads.
+  __shared__ __attribute__((aligned(1024))) char R0[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R1[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R2[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R3[kWaves * RG::SLOTB];
+  auto rslot = [&](auto I) __attribute__((always_inline)) -> char* {
+    constexpr int v = decltype(I)::value;
+    if constexpr (v == 0) return R0;
+    else if constexpr (v == 1) return R1;
+    else if constexpr (v == 2) return R2;
+    else return R3;
+  };
+  static_assert(kRing == 4, "four slot arrays");
   __shared__ float sm[kWaves][T::RPW], sl[kWaves][T::RPW];
   __shared__ float sacc[kWaves][64][kCols + 1];
   const int tid = wi_id();
@@ -97,8 +131,8 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
   const int qi = r0 + r;
   const bool valid = qi < Lq;
   const size_t qrow = (size_t)bh * Lq + (valid ? qi : 0);
-  const float* Kb = K + (size_t)bh * Lk * D + cc * kCols;
-  const float* Vb = V + (size_t)bh * Lk * D + cc * kCols;
+  const auto rk = make_rsrc(K + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
+  const auto rv = make_rsrc(V + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
 
   float q[kCols], acc[kCols];
   load_cols(Q + qrow * D + cc * kCols, q);
@@ -108,14 +142,46 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
   const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
   int k_lo, k_hi;
   wave_part(kend, w, k_lo, k_hi);
+  const int nch = (k_hi - k_lo + RG::CH - 1) / RG::CH;
+
+  // Chunk ch of the part into its slot: lane l of load i moves the 16 bytes
+  // of row i*RPI + l/(D/4), column block l%(D/4), to slot byte 1024 i + 16 l
+  // (rows in order, D floats each).  Chunks past the last re-fetch the last
+  // one (rows past the part repeat its last row), which keeps the loads in
+  // flight the same every iteration.
+  const int lrow = lane / (D / 4), lcol = (lane % (D / 4)) * 16;
+  auto fetch = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    // The resources go to the builtin through local references: passing the
+    // by-reference captures themselves makes the host pass drop this
+    // kernel's launch stub, with no diagnostic.
+    const __amdgpu_buffer_rsrc_t& rkr = rk;
+    const __amdgpu_buffer_rsrc_t& rvr = rv;
+    const int c0 = k_lo + min(ch, nch - 1) * RG::CH;
+    char* slot = rslot(Sc) + w * RG::SLOTB;
+    static_for<0, RG::LPC>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      const int row = min(c0 + i * RG::RPI + lrow, k_hi - 1);
+      const uint32_t off = (uint32_t)row * RG::ROWB + lcol;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkr, (lds_void*)(slot + i * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rvr, (lds_void*)(slot + RG::CHB + i * 1024), 16, off,
+                                               0, 0, 0);
+    });
+  };
+
   float m = -INFINITY, l = 0.f;
-  for (int j0 = k_lo; j0 < k_hi; j0 += kGroup) {
+  auto step = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    fetch(IC<(S + kRing - 1) % kRing>{}, ch + kRing - 1);
+    wait_vm<(kRing - 1) * 2 * RG::LPC>();  // chunk ch landed
+    asm volatile("" ::: "memory");
+    const float* kb = reinterpret_cast<const float*>(rslot(Sc) + w * RG::SLOTB);
+    const float* vb = kb + RG::CHB / 4;
+    const int j0 = k_lo + ch * RG::CH;
     float kv[kGroup][kCols], vv[kGroup][kCols], t[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      const int j = min(j0 + g, k_hi - 1);  // past the part: a repeated, masked row
-      load_cols(Kb + (size_t)j * D, kv[g]);
-      load_cols(Vb + (size_t)j * D, vv[g]);
+      load_cols(kb + g * D + cc * kCols, kv[g]);
+      load_cols(vb + g * D + cc * kCols, vv[g]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -144,6 +210,21 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
 #pragma unroll
       for (int i = 0; i < kCols; ++i) acc[i] = fmaf(p, vv[g][i], acc[i]);
     }
+  };
+  if (nch > 0) {
+    fetch(IC<0>{}, 0);
+    fetch(IC<1>{}, 1);
+    fetch(IC<2>{}, 2);
+    for (int ch = 0; ch < nch; ch += kRing) {
+      step(IC<0>{}, ch);
+      if (ch + 1 >= nch) break;
+      step(IC<1>{}, ch + 1);
+      if (ch + 2 >= nch) break;
+      step(IC<2>{}, ch + 2);
+      if (ch + 3 >= nch) break;
+      step(IC<3>{}, ch + 3);
+    }
+    wait_vm<0>();  // no load into the ring outlives the kernel's use of LDS
   }
   // Merge the four parts: M = max_w m_w, l = sum_w l_w 2^(m_w - M),
   // acc = sum_w acc_w 2^(m_w - M), in wave order.

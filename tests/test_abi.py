@@ -54,6 +54,16 @@ def test_exports_are_only_the_c_api():
     assert text == set(_lib.EXPORTS), text
 
 
+def test_every_kernel_launch_stub_is_defined():
+    # A kernel whose host-side launch stub the compiler dropped (it has done
+    # so silently for some lambda captures passed to buffer-load builtins)
+    # leaves an undefined __device_stub__ symbol: the launch would fail only
+    # when the library is loaded on a GPU machine.
+    out = os.popen(f"nm -D --undefined-only {_lib.LIB_PATH}").read()
+    missing = [l.split()[-1] for l in out.splitlines() if "__device_stub__" in l]
+    assert not missing, missing
+
+
 def test_version(lib):
     assert lib.fa_version().decode().startswith("libfa ")
     assert "gfx950" in lib.fa_version().decode()
