@@ -528,22 +528,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     if (t < nrun) step(IC<0>{}, std::false_type{}, t);
   }
 
-  // dK = scale * dK^T accumulator, dV = dV^T accumulator, one key row per lane.
-  const auto rdk = make_rsrc(dK + koff, (uint32_t)Lk * D * 2);
-  const auto rdv = make_rsrc(dV + koff, (uint32_t)Lk * D * 2);
+  // dK = scale * dK^T accumulator, dV = dV^T accumulator, staged for
+  // whole-row stores in the query-tile buffers (no wave reads them after the
+  // last step's barrier): waves 0 and 1 use Q0 and G0, waves 2 and 3 Q1 and G1.
+  static_assert(2 * 32 * T::ROWB == T::QTB, "two waves' rows per query-tile buffer");
+  u32x2 pk[T::DB][4], pv[T::DB][4];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t off = (uint32_t)(key * D + db * 32 + 8 * g + 4 * h) * 2;
-      u32x2 vk, vv;
-      vk.x = pack_bf16x2(scale * dkacc[db][4 * g + 0], scale * dkacc[db][4 * g + 1]);
-      vk.y = pack_bf16x2(scale * dkacc[db][4 * g + 2], scale * dkacc[db][4 * g + 3]);
-      vv.x = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
-      vv.y = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-      store8(rdk, off, vk);
-      store8(rdv, off, vv);
+      pk[db][g].x = pack_bf16x2(scale * dkacc[db][4 * g + 0], scale * dkacc[db][4 * g + 1]);
+      pk[db][g].y = pack_bf16x2(scale * dkacc[db][4 * g + 2], scale * dkacc[db][4 * g + 3]);
+      pv[db][g].x = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
+      pv[db][g].y = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
     }
+  const int sto = (w & 1) * 32 * T::ROWB;
+  store_rows_staged<D>((w < 2 ? Q0 : Q1) + sto, lane, pk, make_rsrc(dK + koff, (uint32_t)Lk * D * 2),
+                       k0 + 32 * w);
+  store_rows_staged<D>((w < 2 ? G0 : G1) + sto, lane, pv, make_rsrc(dV + koff, (uint32_t)Lk * D * 2),
+                       k0 + 32 * w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1031,22 +1034,24 @@ __global__ __launch_bounds__((64 * DqTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1
   }
   }  // !SPARSE || nkt > 0
   wait_vm<0>();  // the loads of the tiles past the last one
+  // Waves that computed to the last tile read its K slot after the final
+  // barrier; the ring is reused below.
+  block_barrier();
 
-  // ---- dQ = scale * accumulator, one query row per lane --------------------------
-  const auto rdq = make_rsrc(dQ + qoff, (uint32_t)Lq * D * 2);
+  // ---- dQ = scale * accumulator, staged for whole-row stores ----------------------
+  // Wave w's 32 rows go through ring slot K_w (waves 0-3) or V_(w-4).
+  static_assert(T::RB == 1 && 32 * 2 * D <= T::TILEB, "one wave's rows per ring slot");
+  u32x2 pq[T::DB][4];
 #pragma unroll
-  for (int rb = 0; rb < T::RB; ++rb) {
-    const int qrow = qw0 + 32 * rb + n;
+  for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 v;
-        v.x = pack_bf16x2(scale * dq[rb][db][4 * g + 0], scale * dq[rb][db][4 * g + 1]);
-        v.y = pack_bf16x2(scale * dq[rb][db][4 * g + 2], scale * dq[rb][db][4 * g + 3]);
-        store8(rdq, (uint32_t)(qrow * D + db * 32 + 8 * g + 4 * h) * 2, v);
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      pq[db][g].x = pack_bf16x2(scale * dq[0][db][4 * g + 0], scale * dq[0][db][4 * g + 1]);
+      pq[db][g].y = pack_bf16x2(scale * dq[0][db][4 * g + 2], scale * dq[0][db][4 * g + 3]);
+    }
+  char* const st = w == 0 ? K0 : w == 1 ? K1 : w == 2 ? K2 : w == 3 ? K3
+                 : w == 4 ? V0 : w == 5 ? V1 : w == 6 ? V2 : V3;
+  store_rows_staged<D>(st, lane, pq, make_rsrc(dQ + qoff, (uint32_t)Lq * D * 2), qw0);
 }
 
 template <int D, bool CAUSAL, int QMODE>

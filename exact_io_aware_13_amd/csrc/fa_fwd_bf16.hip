@@ -697,16 +697,23 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
           store16(ro, (uint32_t)(qg * D + db * 32 + 8 * g4 + 4 * h) * 4, v);
         }
     } else {
-      const auto ro = make_rsrc(static_cast<uint16_t*>(O) + qoff, (uint32_t)Lq * D * 2);
+      // bf16 O is staged for whole-row stores in the wave's ring slot (K_w,
+      // or V_(w-4)).  Waves that computed to the last tile read its V slot
+      // after the final barrier, so all waves meet once more first.
+      static_assert(T::RB == 1 && 32 * 2 * D <= T::TILEB, "one wave's rows per ring slot");
+      block_barrier();
+      u32x2 po[T::DB][4];
 #pragma unroll
       for (int db = 0; db < T::DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 v;
-          v.x = pack_bf16x2(oacc[rb][db][4 * g4 + 0] * inv, oacc[rb][db][4 * g4 + 1] * inv);
-          v.y = pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv);
-          store8(ro, (uint32_t)(qg * D + db * 32 + 8 * g4 + 4 * h) * 2, v);
+          po[db][g4].x = pack_bf16x2(oacc[rb][db][4 * g4 + 0] * inv, oacc[rb][db][4 * g4 + 1] * inv);
+          po[db][g4].y = pack_bf16x2(oacc[rb][db][4 * g4 + 2] * inv, oacc[rb][db][4 * g4 + 3] * inv);
         }
+      char* const st = w == 0 ? K0 : w == 1 ? K1 : w == 2 ? K2 : w == 3 ? K3
+                     : w == 4 ? V0 : w == 5 ? V1 : w == 6 ? V2 : V3;
+      store_rows_staged<D>(st, lane, po, make_rsrc(static_cast<uint16_t*>(O) + qoff, (uint32_t)Lq * D * 2),
+                           qw0);
     }
     if (h == 0 && qg < Lq)
       LSE[(size_t)bh * Lq + qg] =

@@ -68,6 +68,44 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Whole-row stores of one wave's 32 output rows of D bf16 columns held in
+// the 32x32 accumulator layout: lane (n = lane % 32, h = lane / 32) holds,
+// for each 32-wide column block db and group g, the 8-byte piece v[db][g] =
+// columns 32db + 8g + 4h .. +3 of row n.  Stored directly, each store
+// instruction would write 16 bytes into each of 32 rows.  The wave instead
+// writes the pieces to its own LDS staging area st (32 * 2D bytes, not read
+// by any other wave) and stores whole rows, 1 KiB per instruction, to rows
+// row0 .. row0 + 31 of the buffer r (rows past its range are dropped by the
+// range check).  It reads back only what it wrote, so no barrier is needed.
+// Staging layout: 8-byte slot s of row r at slot s ^ x(r), x(r) = (r / rows
+// per 256-byte bank line) mod slots per row, which spreads the 32 lanes of
+// a write over all banks; a 16-byte chunk c then sits at chunk c ^ (x >> 1),
+// its halves swapped when x is odd.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(char* st, int lane, const u32x2 (&v)[D / 32][4],
+                                                  __amdgpu_buffer_rsrc_t r, int row0) {
+  constexpr int ROWB = 2 * D;           // bytes per row
+  constexpr int SLOTS = D / 4;          // 8-byte slots per row
+  constexpr int RPL = 256 / ROWB;       // rows per 256-byte bank line
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPK = 1024 / ROWB;      // rows per 1-KiB store instruction
+  const int n = lane & 31, h = lane >> 5;
+  const int xw = (n / RPL) & (SLOTS - 1);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<u32x2*>(st + n * ROWB + (((8 * db + 2 * g + h) ^ xw) << 3)) = v[db][g];
+#pragma unroll
+  for (int i = 0; i < 32 * ROWB / 1024; ++i) {
+    const int rr = i * RPK + lane / CPR, cl = lane % CPR;
+    const int xr = (rr / RPL) & (SLOTS - 1);
+    u32x4 a = *reinterpret_cast<const u32x4*>(st + rr * ROWB + ((cl ^ (xr >> 1)) << 4));
+    if (xr & 1) a = u32x4{a.z, a.w, a.x, a.y};
+    store16(r, (uint32_t)((row0 + rr) * D + cl * 8) * 2, a);
+  }
+}
+
 // Row max / row sum across the two wave halves (lanes l and l ^ 32 hold the
 // two halves of one query row).  v_permlane32_swap exchanges the upper 32
 // lanes of its first operand with the lower 32 lanes of its second; applied
