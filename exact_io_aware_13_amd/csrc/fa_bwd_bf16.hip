@@ -69,44 +69,65 @@ namespace {
 // 1. D statistic (stored negated) and base-2 lse
 // ---------------------------------------------------------------------------
 // O_F32: O is the fp32 output of the forward's fp32-output variant (dO stays
-// bf16); D is summed in fp32 either way.
-template <int D, bool O_F32>
+// bf16); D is summed in fp32 either way.  A row takes D/8 lanes, 8 elements
+// each.  NT (large bf16 tensors): each thread takes two rows, issuing all
+// their loads first, and the O and dO loads carry the non-temporal hint --
+// they are read once here (B1 H32 L4096 d128: 11.8 -> 10.2 us); tensors small
+// enough to stay in the last-level cache between calls measured slower with
+// the hint, and the second row alone gained nothing.
+template <int D, bool NT>
+constexpr int pre_rows_per_block() { return (NT ? 2 : 1) * 256 / (D / 8); }
+
+template <int D, bool O_F32, bool NT>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
     const void* __restrict__ O, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse, float* __restrict__ Dvec, float* __restrict__ lse2,
     int64_t rows) {
-  constexpr int LPR = D / 8;        // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;    // rows per workgroup
-  const int64_t row = (int64_t)wg_id() * RPB + wi_id() / LPR;
+  constexpr int LPR = D / 8;          // lanes per row, 8 elements each
+  constexpr int RPP = 256 / LPR;      // rows per pass of the workgroup
+  constexpr int NR = NT ? 2 : 1;      // rows per thread
   const int c = wi_id() % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * D + c * 8);
-    float o8[8];
+  auto ld = [](const auto* p) __attribute__((always_inline)) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+  };
+  u32x4 g[NR];
+  float o8[NR][8];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int64_t row = ((int64_t)wg_id() * NR + u) * RPP + wi_id() / LPR;
+    const int64_t r = row < rows ? row : rows - 1;  // past the end: a repeated row, not stored
+    g[u] = ld(reinterpret_cast<const u32x4*>(dO + r * D + c * 8));
     if constexpr (O_F32) {
-      const f32x4* op = reinterpret_cast<const f32x4*>(static_cast<const float*>(O) + row * D + c * 8);
-      const f32x4 a = op[0], b = op[1];
+      const f32x4* op = reinterpret_cast<const f32x4*>(static_cast<const float*>(O) + r * D + c * 8);
+      const f32x4 a = ld(op), b = ld(op + 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o8[i] = a[i];
-        o8[4 + i] = b[i];
+        o8[u][i] = a[i];
+        o8[u][4 + i] = b[i];
       }
     } else {
-      const u32x4 o = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(O) + row * D + c * 8);
+      const u32x4 o = ld(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(O) + r * D + c * 8));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o8[2 * i] = bf16_lo(o[i]);
-        o8[2 * i + 1] = bf16_hi(o[i]);
+        o8[u][2 * i] = bf16_lo(o[i]);
+        o8[u][2 * i + 1] = bf16_hi(o[i]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc += o8[2 * i] * bf16_lo(g[i]) + o8[2 * i + 1] * bf16_hi(g[i]);
   }
 #pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && c == 0) {
-    Dvec[row] = -acc;
-    lse2[row] = lse[row] * kLog2e;
+  for (int u = 0; u < NR; ++u) {
+    const int64_t row = ((int64_t)wg_id() * NR + u) * RPP + wi_id() / LPR;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += o8[u][2 * i] * bf16_lo(g[u][i]) + o8[u][2 * i + 1] * bf16_hi(g[u][i]);
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && c == 0) {
+      Dvec[row] = -acc;
+      lse2[row] = lse[row] * kLog2e;
+    }
   }
 }
 
@@ -1082,14 +1103,20 @@ template <int D>
 hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Lq;
   if ((stages & kBwdPrepare) && rows > 0) {
-    constexpr int RPB = 256 / (D / 8);
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+    // The NT variant once bf16 O and dO together reach 64 MiB (with fp32 O
+    // it measured no faster).
+    const bool nt = !a.o_f32 && rows * D * 4 >= (int64_t(64) << 20);
+    const auto* G = static_cast<const uint16_t*>(a.dO);
+    auto grid = [&](int rpb) { return dim3((unsigned)((rows + rpb - 1) / rpb)); };
     if (a.o_f32)
-      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, true>), grid, dim3(256), 0, stream, a.O,
-                         static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, true, false>), grid(pre_rows_per_block<D, false>()),
+                         dim3(256), 0, stream, a.O, G, a.lse, a.Dvec, a.lse2, rows);
+    else if (nt)
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false, true>), grid(pre_rows_per_block<D, true>()),
+                         dim3(256), 0, stream, a.O, G, a.lse, a.Dvec, a.lse2, rows);
     else
-      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false>), grid, dim3(256), 0, stream, a.O,
-                         static_cast<const uint16_t*>(a.dO), a.lse, a.Dvec, a.lse2, rows);
+      hipLaunchKernelGGL((bwd_pre_bf16_kernel<D, false, false>), grid(pre_rows_per_block<D, false>()),
+                         dim3(256), 0, stream, a.O, G, a.lse, a.Dvec, a.lse2, rows);
   }
   // dQ: 256-row workgroups unless that gives fewer than two per compute
   // unit; then 128-row ones (as the forward).
