@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restric
 
 // ---------------------------------------------------------------------------
 // dK and dV: a workgroup owns RPW key rows; its waves split the queries that
-// can see them, and the four partial sums are added in wave order.
+// can see them, and the four partial sums are added in wave order.  Each
+// wave streams its query rows (Q, dO, and the rows' base-2 lse and D)
+// through a private LDS ring as the forward streams keys.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
@@ -283,6 +285,19 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     float* __restrict__ dK, float* __restrict__ dV, int BH, int Lq, int Lk, float c,
     float scale) {
   using T = F32Tile<D>;
+  using RG = F32Ring<D>;
+  constexpr int SB = RG::SLOTB + 32;  // Q rows, dO rows, 4 lse2, 4 D
+  __shared__ __attribute__((aligned(1024))) char R0[kWaves * SB];
+  __shared__ __attribute__((aligned(1024))) char R1[kWaves * SB];
+  __shared__ __attribute__((aligned(1024))) char R2[kWaves * SB];
+  __shared__ __attribute__((aligned(1024))) char R3[kWaves * SB];
+  auto rslot = [&](auto I) __attribute__((always_inline)) -> char* {
+    constexpr int v = decltype(I)::value;
+    if constexpr (v == 0) return R0;
+    else if constexpr (v == 1) return R1;
+    else if constexpr (v == 2) return R2;
+    else return R3;
+  };
   __shared__ float sk[kWaves][64][kCols + 1], sv[kWaves][64][kCols + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,25 +315,59 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     ak[i] = 0.f;
     av[i] = 0.f;
   }
-  const float* Qb = Q + (size_t)bh * Lq * D + cc * kCols;
-  const float* Gb = dO + (size_t)bh * Lq * D + cc * kCols;
-  const float* Lb = LSE2 + (size_t)bh * Lq;
-  const float* Db = Dvec + (size_t)bh * Lq;
+  const auto rq = make_rsrc(Q + (size_t)bh * Lq * D, (uint32_t)Lq * RG::ROWB);
+  const auto rg = make_rsrc(dO + (size_t)bh * Lq * D, (uint32_t)Lq * RG::ROWB);
+  const auto rl = make_rsrc(LSE2 + (size_t)bh * Lq, (uint32_t)Lq * 4);
+  const auto rd = make_rsrc(Dvec + (size_t)bh * Lq, (uint32_t)Lq * 4);
   // Queries that can see a key of this workgroup, split over the waves.
   const int qstart = CAUSAL ? min(Lq, k0) : 0;
   int q_lo, q_hi;
   wave_part(Lq - qstart, w, q_lo, q_hi);
   q_lo += qstart;
   q_hi += qstart;
-  for (int i0 = q_lo; i0 < q_hi; i0 += kGroup) {
-    float qv[kGroup][kCols], gv[kGroup][kCols], lv[kGroup], dv[kGroup];
+  const int nch = (q_hi - q_lo + RG::CH - 1) / RG::CH;
+
+  // Chunk ch of the part into its slot (the forward's layout for the rows;
+  // lanes 0-3 then move the chunk's four lse2 and four D values, rows past
+  // Lq reading as zero).  The resources go to the builtin through local
+  // references (see the forward).
+  const int lrow = lane / (D / 4), lcol = (lane % (D / 4)) * 16;
+  auto fetch = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t& rqr = rq;
+    const __amdgpu_buffer_rsrc_t& rgr = rg;
+    const __amdgpu_buffer_rsrc_t& rlr = rl;
+    const __amdgpu_buffer_rsrc_t& rdr = rd;
+    const int c0 = q_lo + min(ch, nch - 1) * RG::CH;
+    char* slot = rslot(Sc) + w * SB;
+    static_for<0, RG::LPC>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      const int row = min(c0 + i * RG::RPI + lrow, q_hi - 1);
+      const uint32_t off = (uint32_t)row * RG::ROWB + lcol;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rqr, (lds_void*)(slot + i * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rgr, (lds_void*)(slot + RG::CHB + i * 1024), 16, off,
+                                               0, 0, 0);
+    });
+    if (lane < RG::CH) {
+      const uint32_t off = (uint32_t)(c0 + lane) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rlr, (lds_void*)(slot + RG::SLOTB), 4, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdr, (lds_void*)(slot + RG::SLOTB + 16), 4, off, 0, 0, 0);
+    }
+  };
+  auto step = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    fetch(IC<(S + kRing - 1) % kRing>{}, ch + kRing - 1);
+    wait_vm<(kRing - 1) * (2 * RG::LPC + 2)>();  // chunk ch landed
+    asm volatile("" ::: "memory");
+    const char* slot = rslot(Sc) + w * SB;
+    const float* qb = reinterpret_cast<const float*>(slot);
+    const float* gb = qb + RG::CHB / 4;
+    const float* st = reinterpret_cast<const float*>(slot + RG::SLOTB);
+    const int i0 = q_lo + ch * RG::CH;
+    float qv[kGroup][kCols], gv[kGroup][kCols];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      const int i = min(i0 + g, q_hi - 1);
-      load_cols(Qb + (size_t)i * D, qv[g]);
-      load_cols(Gb + (size_t)i * D, gv[g]);
-      lv[g] = Lb[i];
-      dv[g] = Db[i];
+      load_cols(qb + g * D + cc * kCols, qv[g]);
+      load_cols(gb + g * D + cc * kCols, gv[g]);
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
@@ -332,14 +381,30 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
       dp = row_sum<T::LPR>(dp);
       const int i = i0 + g;
       const bool vis = i < q_hi && !(CAUSAL && i < kj);
-      const float p = vis ? exp2f(s * c - lv[g]) : 0.f;
-      const float ds = p * (dp - dv[g]);
+      const float p = vis ? exp2f(s * c - st[g]) : 0.f;
+      const float ds = p * (dp - st[4 + g]);
 #pragma unroll
       for (int x = 0; x < kCols; ++x) {
         av[x] = fmaf(p, gv[g][x], av[x]);
         ak[x] = fmaf(ds, qv[g][x], ak[x]);
       }
     }
+  };
+  static_assert(RG::CH == 4 && kGroup == 4, "four rows of lse2 and D per chunk");
+  if (nch > 0) {
+    fetch(IC<0>{}, 0);
+    fetch(IC<1>{}, 1);
+    fetch(IC<2>{}, 2);
+    for (int ch = 0; ch < nch; ch += kRing) {
+      step(IC<0>{}, ch);
+      if (ch + 1 >= nch) break;
+      step(IC<1>{}, ch + 1);
+      if (ch + 2 >= nch) break;
+      step(IC<2>{}, ch + 2);
+      if (ch + 3 >= nch) break;
+      step(IC<3>{}, ch + 3);
+    }
+    wait_vm<0>();
   }
 #pragma unroll
   for (int x = 0; x < kCols; ++x) {
@@ -368,7 +433,8 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ: a workgroup owns RPW query rows; its waves split the keys they see, and
-// the four partial sums are added in wave order.
+// the four partial sums are added in wave order.  Keys stream through a
+// private LDS ring per wave, as in the forward.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
@@ -376,6 +442,18 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     float* __restrict__ dQ, int BH, int Lq, int Lk, float c, float scale) {
   using T = F32Tile<D>;
+  using RG = F32Ring<D>;
+  __shared__ __attribute__((aligned(1024))) char R0[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R1[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R2[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R3[kWaves * RG::SLOTB];
+  auto rslot = [&](auto I) __attribute__((always_inline)) -> char* {
+    constexpr int v = decltype(I)::value;
+    if constexpr (v == 0) return R0;
+    else if constexpr (v == 1) return R1;
+    else if constexpr (v == 2) return R2;
+    else return R3;
+  };
   __shared__ float sq[kWaves][64][kCols + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -392,18 +470,40 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
   for (int i = 0; i < kCols; ++i) aq[i] = 0.f;
   const float lse2 = LSE2[qrow];
   const float Di = Dvec[qrow];
-  const float* Kb = K + (size_t)bh * Lk * D + cc * kCols;
-  const float* Vb = V + (size_t)bh * Lk * D + cc * kCols;
+  const auto rk = make_rsrc(K + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
+  const auto rv = make_rsrc(V + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
   const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
   int k_lo, k_hi;
   wave_part(kend, w, k_lo, k_hi);
-  for (int j0 = k_lo; j0 < k_hi; j0 += kGroup) {
+  const int nch = (k_hi - k_lo + RG::CH - 1) / RG::CH;
+  const int lrow = lane / (D / 4), lcol = (lane % (D / 4)) * 16;
+  auto fetch = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t& rkr = rk;
+    const __amdgpu_buffer_rsrc_t& rvr = rv;
+    const int c0 = k_lo + min(ch, nch - 1) * RG::CH;
+    char* slot = rslot(Sc) + w * RG::SLOTB;
+    static_for<0, RG::LPC>([&](auto Ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(Ic)::value;
+      const int row = min(c0 + i * RG::RPI + lrow, k_hi - 1);
+      const uint32_t off = (uint32_t)row * RG::ROWB + lcol;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rkr, (lds_void*)(slot + i * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rvr, (lds_void*)(slot + RG::CHB + i * 1024), 16, off,
+                                               0, 0, 0);
+    });
+  };
+  auto step = [&](auto Sc, int ch) __attribute__((always_inline)) {
+    constexpr int S = decltype(Sc)::value;
+    fetch(IC<(S + kRing - 1) % kRing>{}, ch + kRing - 1);
+    wait_vm<(kRing - 1) * 2 * RG::LPC>();  // chunk ch landed
+    asm volatile("" ::: "memory");
+    const float* kb = reinterpret_cast<const float*>(rslot(Sc) + w * RG::SLOTB);
+    const float* vb = kb + RG::CHB / 4;
+    const int j0 = k_lo + ch * RG::CH;
     float kv[kGroup][kCols], vv[kGroup][kCols];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      const int j = min(j0 + g, k_hi - 1);
-      load_cols(Kb + (size_t)j * D, kv[g]);
-      load_cols(Vb + (size_t)j * D, vv[g]);
+      load_cols(kb + g * D + cc * kCols, kv[g]);
+      load_cols(vb + g * D + cc * kCols, vv[g]);
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
@@ -421,6 +521,21 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
 #pragma unroll
       for (int x = 0; x < kCols; ++x) aq[x] = fmaf(ds, kv[g][x], aq[x]);
     }
+  };
+  if (nch > 0) {
+    fetch(IC<0>{}, 0);
+    fetch(IC<1>{}, 1);
+    fetch(IC<2>{}, 2);
+    for (int ch = 0; ch < nch; ch += kRing) {
+      step(IC<0>{}, ch);
+      if (ch + 1 >= nch) break;
+      step(IC<1>{}, ch + 1);
+      if (ch + 2 >= nch) break;
+      step(IC<2>{}, ch + 2);
+      if (ch + 3 >= nch) break;
+      step(IC<3>{}, ch + 3);
+    }
+    wait_vm<0>();
   }
 #pragma unroll
   for (int x = 0; x < kCols; ++x) sq[w][lane][x] = aq[x];
