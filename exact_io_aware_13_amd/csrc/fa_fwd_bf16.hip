@@ -127,25 +127,33 @@ struct FwdTile {
 // MODE: 0 dense, 256 rows per workgroup; 1 dense, 128 rows; 2 block-sparse,
 // 128 rows.
 template <int D, bool CAUSAL, bool OUT_F32, int MODE>
-__global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1)) void fwd_bf16_kernel(
+__global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 1)),
+                             ((MODE == 1 || MODE == 2) ? 2 : 1)) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ O, float* __restrict__ LSE,
     int BH, int Lq, int Lk, int n_qt, float c, unsigned qsign,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = FwdTile<D, MODE != 0>;
   constexpr bool SPARSE = MODE == 2;
+  // MODE 3: 128 query rows and two groups of four waves; group g takes the
+  // g-th half of the workgroup's key tiles for the same rows (its own half of
+  // every ring slot), and the halves' (reference, sum, accumulator) are
+  // merged in LDS at the end.  This halves the longest chain of key tiles,
+  // which bounds short causal launches.
+  constexpr bool SPLIT = MODE == 3;
+  constexpr int NG = SPLIT ? 2 : 1;
   // Quarter priorities within each iteration (see the product loop): for
   // 256-row workgroups, and for 128-row ones without the causal mask, where
   // they measured faster; causal 128-row launches measured slower.
-  constexpr bool PRIO = MODE == 0 || (MODE == 1 && !CAUSAL);
-  __shared__ __attribute__((aligned(1024))) char K0[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char K1[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char K2[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char K3[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char V0[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char V1[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char V2[T::TILEB];
-  __shared__ __attribute__((aligned(1024))) char V3[T::TILEB];
+  constexpr bool PRIO = MODE == 0 || MODE == 3 || (MODE == 1 && !CAUSAL);
+  __shared__ __attribute__((aligned(1024))) char K0[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char K1[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char K2[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char K3[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char V0[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char V1[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char V2[T::TILEB * NG];
+  __shared__ __attribute__((aligned(1024))) char V3[T::TILEB * NG];
   auto kslot = [&](auto I) __attribute__((always_inline)) -> char* {
     constexpr int v = decltype(I)::value;
     if constexpr (v == 0) return K0;
@@ -166,6 +174,10 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   // compiler so, which keeps everything derived from it in scalar registers.
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, n = lane & 31, h = lane >> 5;
+  // Key-half group and the wave's index within it (its row block).
+  const int grp = SPLIT ? w / T::NW : 0;
+  const int wr = SPLIT ? w % T::NW : w;
+  const int gofs = grp * T::TILEB;  // the group's half of every ring slot
 
   // Consecutive workgroups take the same query tile of different slices; for
   // causal masks the tiles with the most visible keys are dispatched first.
@@ -182,7 +194,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
       qt = n_qt - 1 - qt;
   }
   const int q0 = qt * T::BR;
-  const int qw0 = q0 + 32 * T::RB * w;  // this wave's first row
+  const int qw0 = q0 + 32 * T::RB * wr;  // this wave's first row
 
   const size_t qoff = (size_t)bh * Lq * D;
   const size_t koff = (size_t)bh * Lk * D;
@@ -236,10 +248,24 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   // issues its share of every tile's loads and joins every barrier (see the
   // drain after the main loop).  The block-sparse workgroup runs its list
   // with every wave.
+  // SPLIT: the group's tiles are tbase .. tbase + nreal - 1, and every wave
+  // of the workgroup iterates over the larger half's count (the same
+  // barriers).  A wave whose rows see no key of its half computes one fully
+  // masked tile (probabilities exactly 0); a half with no tile at all is
+  // left out of the merge.
+  const int nkt_all = nkt;
+  int tbase = 0, nreal = nkt;
+  if constexpr (SPLIT) {
+    const int half = (nkt + 1) / 2;
+    tbase = grp ? half : 0;
+    nreal = grp ? nkt - half : half;
+    nkt = half;
+  }
   int nkt_w = nkt;
   if constexpr (!SPARSE) {
-    if (CAUSAL) nkt_w = min(nkt, (qw0 + 32 * T::RB - 1) / T::BC + 1);
-    if (qw0 >= Lq) nkt_w = 1;
+    if (CAUSAL) nkt_w = min(nkt, (qw0 + 32 * T::RB - 1) / T::BC + 1 - tbase);
+    if constexpr (SPLIT) nkt_w = min(nkt_w, nreal);
+    if (qw0 >= Lq || nkt_w < 1) nkt_w = 1;
   }
   // Key tile of loop position j (the window must hold entry j / TPB).
   auto tile_at = [&](int j) __attribute__((always_inline)) -> int {
@@ -250,6 +276,8 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
       const unsigned src = e < 64 ? win0 : win1;
       const int kb = __builtin_amdgcn_readlane((int)src, e & 63);
       return kb * TPB + j % TPB;
+    } else if constexpr (SPLIT) {
+      return tbase + min(j, nreal - 1);
     } else {
       return j;
     }
@@ -272,7 +300,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   int fetch_off[T::LOADS];
 #pragma unroll
   for (int i = 0; i < T::LOADS; ++i) {
-    const int row = (w * T::LOADS + i) * T::RPK + lane / T::CPR;
+    const int row = (wr * T::LOADS + i) * T::RPK + lane / T::CPR;
     const int chunk = (lane % T::CPR) ^ swz<D>(row);
     fetch_off[i] = (row * D + chunk * 8) * 2;
   }
@@ -284,7 +312,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
     // swizzled chunk, carried by the per-lane offset): one LDS base for the
     // wave's loads, the rest in the immediate offset.
     const int t = tile_at(min(tile, nkt - 1));
-    lds_void* dst = (lds_void*)(slot + w * T::LOADS * 1024);
+    lds_void* dst = (lds_void*)(slot + gofs + wr * T::LOADS * 1024);
     static_for<0, T::LOADS>([&](auto Ic) __attribute__((always_inline)) {
       constexpr int i = decltype(Ic)::value;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -418,8 +446,8 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
                   unsigned (&pk_cur)[T::RB][T::NKB][8]) __attribute__((always_inline)) {
     constexpr int R = decltype(Rc)::value;
     constexpr bool FIRST = decltype(FIRSTc)::value;
-    const char* kb = kslot(IC<(R + 1) % 4>{});  // K[j+1]
-    const char* vb = vslot(IC<(R + 3) % 4>{});  // V[j-1]
+    const char* kb = kslot(IC<(R + 1) % 4>{}) + gofs;  // K[j+1]
+    const char* vb = vslot(IC<(R + 3) % 4>{}) + gofs;  // V[j-1]
 
     // K[j+1] and V[j-1] were fetched three iterations ahead and waited for
     // at the end of iteration j-1.  This iteration refills the slots of K[j]
@@ -623,7 +651,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   fetch(rv, 1, V1);
   wait_vm<4 * T::LOADS>();  // K0 and K1 landed
   block_barrier();
-  score_tile(K0, sA);
+  score_tile(K0 + gofs, sA);
   block_barrier();  // every wave is done with K0 before iteration 0 refills its slot
 
   iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB);
@@ -645,10 +673,10 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   auto last_value = [&]() __attribute__((always_inline)) {
     const unsigned(&plast)[T::RB][T::NKB][8] = ((nkt_w - 1) & 1) ? pA : pB;
     switch ((nkt_w - 1) & 3) {
-      case 0: value_tile(V0, plast); break;
-      case 1: value_tile(V1, plast); break;
-      case 2: value_tile(V2, plast); break;
-      default: value_tile(V3, plast); break;
+      case 0: value_tile(V0 + gofs, plast); break;
+      case 1: value_tile(V1 + gofs, plast); break;
+      case 2: value_tile(V2 + gofs, plast); break;
+      default: value_tile(V3 + gofs, plast); break;
     }
   };
   if (nkt_w == nkt) {
@@ -676,6 +704,41 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
   }
   }  // !SPARSE || nkt > 0
 
+  if constexpr (SPLIT) {
+    // ---- merge of the two key halves --------------------------------------------
+    // Group 1's wave r writes its (reference, sum, accumulator) lane by lane
+    // into ring slots K_r and V_r; group 0's wave r, which holds the same
+    // rows, combines them with its own: M = max(m0, m1), l = l0 2^(m0-M) +
+    // l1 2^(m1-M), acc likewise (always in this order).  The first barrier
+    // covers the last value products' slot reads.
+    static_assert(T::RB == 1 && T::DB * 16 * 64 * 4 <= NG * T::TILEB, "accumulator fits a slot");
+    block_barrier();
+    float* const kw = reinterpret_cast<float*>(wr == 0 ? K0 : wr == 1 ? K1 : wr == 2 ? K2 : K3);
+    float* const vw = reinterpret_cast<float*>(wr == 0 ? V0 : wr == 1 ? V1 : wr == 2 ? V2 : V3);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) kw[(db * 16 + r) * 64 + lane] = oacc[0][db][r];
+      vw[lane] = m[0];
+      vw[64 + lane] = l[0];
+    }
+    block_barrier();
+    if (grp == 1) return;  // no barrier follows
+    if (nkt_all - nkt > 0) {  // the second half had tiles
+      const float m1 = vw[lane], l1 = vw[64 + lane];
+      const float M = fmaxf(m[0], m1);
+      const float a0 = fast_exp2(m[0] - M), a1 = fast_exp2(m1 - M);
+      l[0] = l[0] * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[0][db][r] = oacc[0][db][r] * a0 + kw[(db * 16 + r) * 64 + lane] * a1;
+      m[0] = M;
+    }
+  }
+
   // ---- epilogue: O = acc / l, lse = (m + log2 l) * ln 2 ---------------------
 #pragma unroll
   for (int rb = 0; rb < T::RB; ++rb) {
@@ -701,7 +764,9 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 
       // or V_(w-4)).  Waves that computed to the last tile read its V slot
       // after the final barrier, so all waves meet once more first.
       static_assert(T::RB == 1 && 32 * 2 * D <= T::TILEB, "one wave's rows per ring slot");
-      block_barrier();
+      // (SPLIT: the merge's barriers already ordered every slot reader, and
+      // group 1 has returned; wave r stages in K_r, which only it reads now.)
+      if constexpr (!SPLIT) block_barrier();
       u32x2 po[T::DB][4];
 #pragma unroll
       for (int db = 0; db < T::DB; ++db)
@@ -731,7 +796,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   float c = fabsf(a.scale) * kLog2e;
   if (c < 1e-30f) c = 1e-30f;
   const unsigned qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MODE>), grid, dim3(64 * T::NW), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_F32, MODE>), grid,
+                     dim3(64 * T::NW * (MODE == 3 ? 2 : 1)), 0,
                      stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                      static_cast<const uint16_t*>(a.V), a.O, a.lse, a.BH, a.Lq, a.Lk, n_qt, c,
                      qsign, a.block_mask, a.bm_stride, a.nqb, a.nkb);
@@ -754,7 +820,17 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   // (gfx950: 256 compute units); then 128-row ones, which also halve the
   // longest workgroup's work under a causal mask.
   const int64_t wgs256 = (int64_t)((a.Lq + 255) / 256) * a.BH;
-  if (wgs256 < 2 * kComputeUnits) return a.d == 64 ? launch_d<64, 1>(a, stream) : launch_d<128, 1>(a, stream);
+  if (wgs256 < 2 * kComputeUnits) {
+    // Causal launches whose longest row tile runs at least 128 key tiles
+    // (the heavy tiles then bound the launch) split each workgroup's keys
+    // over two wave groups: B1 H8 L8192 d128 140.4 -> 133.2 us.  Shorter
+    // ones keep two 128-row workgroups per compute unit (the split's 128 KiB
+    // of LDS allows one): B2 H16 L2048 d128 40.8 us against 42.3.
+    const int bc = a.d == 128 ? FwdTile<128, true>::BC : FwdTile<64, true>::BC;
+    if (a.causal && (a.Lk + bc - 1) / bc >= 128)
+      return a.d == 64 ? launch_d<64, 3>(a, stream) : launch_d<128, 3>(a, stream);
+    return a.d == 64 ? launch_d<64, 1>(a, stream) : launch_d<128, 1>(a, stream);
+  }
   return a.d == 64 ? launch_d<64, 0>(a, stream) : launch_d<128, 0>(a, stream);
 }
 

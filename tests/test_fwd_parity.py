@@ -127,6 +127,31 @@ def test_long_context_workload_sampled_rows():
     assert_bf16_fwd(fwd_errors(Og, lg, O_ref, lse_ref), w.name)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 4100, 4100, 128), (1, 2, 8200, 8200, 64),
+                                   (1, 2, 3000, 4500, 128), (1, 1, 5000, 4097, 128)],
+                         ids=lambda s: "B{}H{}Lq{}Lk{}d{}".format(*s))
+def test_split_key_halves_long_causal(shape):
+    # Few workgroups and at least 128 key tiles: the launch splits each
+    # workgroup's keys over two wave groups and merges them.  256 seeded
+    # rows per head (the first and last included), plus one full head.
+    B, H, Lq, Lk, d = shape
+    q, k, v = make_inputs(B, H, Lq, Lk, d, "bf16", seed=Lq + Lk + d)
+    scale = 1.0 / math.sqrt(d)
+    announce(f"fwd bf16 split halves {shape}")
+    O, lse = fa.fa_fwd(*to_dev(q, k, v), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    O, lse = f64(O), f64(lse)
+    qd, kd, vd = f64(q), f64(k), f64(v)
+    rows = sample_rows(H=H, L=Lq, n=256, seed=d).numpy()
+    O_ref, lse_ref = oracle.attn_fwd_rows(qd, kd, vd, scale, True, rows)
+    Og = np.take_along_axis(O, rows[..., None], axis=2)
+    lg = np.take_along_axis(lse, rows, axis=2)
+    assert_bf16_fwd(fwd_errors(Og, lg, O_ref, lse_ref), f"{shape} sampled rows")
+    if Lq * Lk <= 4100 * 4100:
+        Oh, lh = oracle.attn_fwd(qd[:, :1], kd[:, :1], vd[:, :1], scale, True)
+        assert_bf16_fwd(fwd_errors(O[:, :1], lse[:, :1], Oh, lh), f"{shape} head 0")
+
+
 def test_constant_values_are_returned_at_full_size():
     # Property that holds at any size: constant V rows give O = that row.
     B, H, L, d = 1, 4, 4096, 128
