@@ -1,9 +1,10 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
 One step is one pass of the whole hot path over one batch through the C ABI:
-fa_fwd (O, lse), then the backward's three stages fa_bwd_prepare (D, base-2
-lse), fa_bwd_dkdv and fa_bwd_dq -- together exactly fa_bwd -- at B1 H32
-L4096 d128, causal, bf16 inputs with fp32 accumulation.  Inputs, outputs and
+fa_fwd (O, lse), then the backward in its two kernels, fa_bwd_prepare_dq (the
+per-row statistics D and base-2 lse, and dQ, in one kernel) and fa_bwd_dkdv
+-- together exactly fa_bwd -- at B1 H32 L4096 d128, causal, bf16 inputs with
+fp32 accumulation.  Inputs, outputs and
 the workspace are resident in device memory before timing starts.
 
 Throughput uses the algorithmic FLOP count: forward 4*B*H*Lq*Lk*d, halved for
@@ -80,8 +81,9 @@ def kernel_table(B, H, L, d):
 
     One matrix product over the visible (query, key) pairs is f1 = fwd / 2.
     The forward does 2 (S, PV); dK/dV does 4 of the backward's 5 (S, dP, dV,
-    dK); dQ does 1 algorithmic product (dQ) plus S and dP again.  Bytes:
-    every tensor the kernel must touch, read or written once.
+    dK); dQ does 1 algorithmic product (dQ) plus S and dP again, and also
+    forms the row statistics (reading O and lse, writing D and base-2 lse).
+    Bytes: every tensor the kernel must touch, read or written once.
     """
     f_fwd, _ = flops(B, H, L, L, d, True)
     f1 = f_fwd / 2
@@ -90,12 +92,10 @@ def kernel_table(B, H, L, d):
     return {
         "fwd_bf16_kernel": dict(src="fa_fwd_bf16.hip", flops=2 * f1, executed=2 * f1,
                                 bytes=3 * t + t + r),
-        "bwd_pre_bf16_kernel": dict(src="fa_bwd_bf16.hip", flops=0.0, executed=0.0,
-                                    bytes=2 * t + r + 2 * r),
         "bwd_dkdv_kernel": dict(src="fa_bwd_bf16.hip", flops=4 * f1, executed=4 * f1,
                                 bytes=4 * t + 2 * r + 2 * t),
         "bwd_dq_kernel": dict(src="fa_bwd_bf16.hip", flops=1 * f1, executed=3 * f1,
-                              bytes=4 * t + 2 * r + t),
+                              bytes=5 * t + r + 2 * r + t),
     }
 
 
@@ -575,16 +575,16 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.fa_bwd_workspace_bytes(torch.bfloat16, B, H, L, L, d), dtype=torch.uint8,
                      device=dev)
-    names = ["fwd_bf16_kernel", "bwd_pre_bf16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"]
+    names = ["fwd_bf16_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]
 
     def step(ev=None):
         # Events go on torch's current stream, the stream every call below
         # launches its kernel on.
         calls = [
             lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=lse),
-            lambda: fa.fa_bwd_prepare(O, do, lse, L, ws),
+            lambda: fa.fa_bwd_prepare_dq(q, k, v, O, do, lse, ws, scale=w.scale, causal=True,
+                                         dq=dq),
             lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, scale=w.scale, causal=True, dk=dk, dv=dv),
-            lambda: fa.fa_bwd_dq(q, k, v, do, ws, scale=w.scale, causal=True, dq=dq),
         ]
         for i, call in enumerate(calls):
             if ev is not None:
@@ -620,7 +620,8 @@ def main():
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
     i_start = torch.cuda.Event(enable_timing=True)
     i_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -647,7 +648,8 @@ def main():
         "fwd_bf16_kernel": lambda: fa.fa_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=lse),
         "bwd_dkdv_kernel": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, scale=w.scale, causal=True,
                                                   dk=dk, dv=dv),
-        "bwd_dq_kernel": lambda: fa.fa_bwd_dq(q, k, v, do, ws, scale=w.scale, causal=True, dq=dq),
+        "bwd_dq_kernel": lambda: fa.fa_bwd_prepare_dq(q, k, v, O, do, lse, ws, scale=w.scale,
+                                                      causal=True, dq=dq),
     })
 
     f_fwd, f_bwd = flops(B, H, L, L, d, True)

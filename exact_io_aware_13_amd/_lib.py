@@ -22,7 +22,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd", "fa_bwd_blocksparse", "fa_bwd_prepare", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
+           "fa_bwd_prepare_dq", "fa_bwd_workspace_bytes", "fa_fwd_splitkv", "fa_fwd_splitkv_partial",
            "fa_fwd_splitkv_merge", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_default_splits", "fa_bwd_noalloc", "fa_bwd_noalloc_max_scratch_bytes",
            "fa_status_str", "fa_version")
@@ -61,6 +61,9 @@ def _declare(lib):
     lib.fa_bwd_dq.restype = i32
     lib.fa_bwd_dq.argtypes = [i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, f32, i32, vp, vp,
                               ctypes.c_size_t, vp]
+    lib.fa_bwd_prepare_dq.restype = i32
+    lib.fa_bwd_prepare_dq.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                      f32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.fa_fwd_splitkv.restype = i32

@@ -1,7 +1,7 @@
 """Python binding of libfa with the C ABI's names.
 
 ``fa_fwd``, ``fa_fwd_blocksparse``, ``fa_bwd`` (and its stages ``fa_bwd_prepare``, ``fa_bwd_dkdv``,
-``fa_bwd_dq``), ``fa_bwd_workspace_bytes`` and the key-split forward
+``fa_bwd_dq``, ``fa_bwd_prepare_dq``), ``fa_bwd_workspace_bytes`` and the key-split forward
 (``fa_fwd_splitkv`` and its stages) only marshal torch tensors
 (device pointers, sizes, the current HIP stream) into the C calls;
 all arithmetic runs in the library's HIP kernels.  PyTorch supplies device
@@ -298,6 +298,26 @@ def fa_bwd_dq(q, k, v, do, workspace, scale=None, causal=False, dq=None):
     st = _lib.load().fa_bwd_dq(_code(q.dtype), B, H, Lq, Lk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(do),
                                float(scale), int(bool(causal)), _ptr(dq), _ptr(workspace),
                                workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return dq
+
+
+def fa_bwd_prepare_dq(q, k, v, o, do, lse, workspace, scale=None, causal=False, dq=None):
+    """Stages 1 and 3 of ``fa_bwd`` in one call (one kernel with bf16 ``o``):
+    the per-row statistics into ``workspace``, and dQ.  ``fa_bwd_dkdv`` can
+    follow it on the same stream."""
+    B, H, Lq, Lk, d, dev = _bwd_shapes(q, k, v, do)
+    _check_tensor("o", o, dev, None, (B, H, Lq, d))
+    _check_tensor("lse", lse, dev, torch.float32, (B, H, Lq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_tensor("dq", dq, dev, q.dtype, q.shape)
+    _check_tensor("workspace", workspace, dev, torch.uint8)
+    st = _lib.load().fa_bwd_prepare_dq(_code(q.dtype), _code(o.dtype), B, H, Lq, Lk, d, _ptr(q),
+                                       _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                       float(scale), int(bool(causal)), _ptr(dq), _ptr(workspace),
+                                       workspace.numel(), _stream(dev))
     _lib.check(st)
     return dq
 

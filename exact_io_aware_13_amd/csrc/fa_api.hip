@@ -249,6 +249,16 @@ fa_status fa_bwd_dq(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64_t
                     stream);
 }
 
+fa_status fa_bwd_prepare_dq(fa_dtype in_dtype, fa_dtype o_dtype, int64_t B, int64_t H,
+                            int64_t Lq, int64_t Lk, int64_t d, const void* Q, const void* K,
+                            const void* V, const void* O, const void* dO, const float* lse,
+                            float scale, int causal, void* dQ, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return bwd_stages(fa::kBwdPrepare | fa::kBwdDq, in_dtype, o_dtype, B, H, Lq, Lk, d, Q, K, V, O,
+                    dO, lse, scale, causal, dQ, nullptr, nullptr, workspace, workspace_bytes,
+                    stream);
+}
+
 }  // extern "C"
 
 namespace {

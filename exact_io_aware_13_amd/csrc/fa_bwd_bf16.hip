@@ -62,6 +62,8 @@
 #include "fa_launch.h"
 #include "fa_tile.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -77,6 +79,21 @@ namespace {
 // the hint, and the second row alone gained nothing.
 template <int D, bool NT>
 constexpr int pre_rows_per_block() { return (NT ? 2 : 1) * 256 / (D / 8); }
+
+// Sum over one 8-element chunk of O[r] * dO[r], one FMA chain in element
+// order.  D is the pairwise sum of a row's chunk sums: chunks c and c ^ s
+// are added for s = D/16, D/32, ..., 1, i.e. the butterfly over the row's
+// lanes below, and the dQ kernel's fused variant adds them in the same
+// order, so both give the same bits.
+__device__ __forceinline__ float chunk_dot8(const float (&o)[8], u32x4 g) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_fmaf(o[2 * i], bf16_lo(g[i]), acc);
+    acc = __builtin_fmaf(o[2 * i + 1], bf16_hi(g[i]), acc);
+  }
+  return acc;
+}
 
 template <int D, bool O_F32, bool NT>
 __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
@@ -118,10 +135,7 @@ __global__ __launch_bounds__(256) void bwd_pre_bf16_kernel(
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int64_t row = ((int64_t)wg_id() * NR + u) * RPP + wi_id() / LPR;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc += o8[u][2 * i] * bf16_lo(g[u][i]) + o8[u][2 * i + 1] * bf16_hi(g[u][i]);
+    float acc = chunk_dot8(o8[u], g[u]);
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (row < rows && c == 0) {
@@ -605,11 +619,16 @@ struct DqTile {
 // 128 rows -- one row block of the mask, visiting the key blocks that row
 // block sees (a compacted list read through register windows, as in the
 // forward).
-template <int D, bool CAUSAL, int MODE>
+// PREP: the kernel also does the prepare kernel's work for its rows -- it
+// reads the bf16 O rows and lse, forms -D and lse2 itself and writes them
+// to Dvec / LSE2 for the dK/dV kernel launched after it (else it reads
+// them there).
+template <int D, bool CAUSAL, int MODE, bool PREP>
 __global__ __launch_bounds__((64 * DqTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1)) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE2, const float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
+    const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ LSE2, float* __restrict__ Dvec, uint16_t* __restrict__ dQ,
     int BH, int Lq, int Lk, int n_qt, float c, float scale,
     const uint8_t* __restrict__ BM, int bm_stride, int nqb, int nkb) {
   using T = DqTile<D, MODE != 0>;
@@ -813,8 +832,44 @@ __global__ __launch_bounds__((64 * DqTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1
       qf[rb][ks] = as_bf16x8(load16(rq, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2));
       gf[rb][ks] = load16(rdo, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2);
     }
-    lse2[rb] = load4f(rl, (uint32_t)qrow * 4);
-    dd[rb] = load4f(re, (uint32_t)qrow * 4);
+    if constexpr (PREP) {
+      // The lane holds chunks c = 2 ks + h of its row (8 elements each) of
+      // dO, and reads the same chunks of O: the chunk sums are combined in
+      // the prepare kernel's pairwise order (c with c ^ 2s, s = KS/2 .. 1,
+      // within the lane; then c with c ^ 1, the other half of the wave).
+      // Rows past Lq read zeros and are not stored.
+      const auto ro = make_rsrc(O + qoff, (uint32_t)Lq * D * 2);
+      const auto rlse = make_rsrc(LSE + (size_t)bh * Lq, (uint32_t)Lq * 4);
+      u32x4 of[T::KS];
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) of[ks] = load16(ro, (uint32_t)(qrow * D + ks * 16 + h * 8) * 2);
+      const float lraw = load4f(rlse, (uint32_t)qrow * 4);
+      float part[T::KS];
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        float o8[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o8[2 * i] = bf16_lo(of[ks][i]);
+          o8[2 * i + 1] = bf16_hi(of[ks][i]);
+        }
+        part[ks] = chunk_dot8(o8, gf[rb][ks]);
+      }
+#pragma unroll
+      for (int st = T::KS / 2; st >= 1; st >>= 1)
+#pragma unroll
+        for (int ks = 0; ks < st; ++ks) part[ks] = part[ks] + part[ks + st];
+      const float dsum = part[0] + __shfl_xor(part[0], 32, 64);
+      lse2[rb] = lraw * kLog2e;
+      dd[rb] = -dsum;
+      if (h == 0 && qrow < Lq) {
+        Dvec[(size_t)bh * Lq + qrow] = dd[rb];
+        LSE2[(size_t)bh * Lq + qrow] = lse2[rb];
+      }
+    } else {
+      lse2[rb] = load4f(rl, (uint32_t)qrow * 4);
+      dd[rb] = load4f(re, (uint32_t)qrow * 4);
+    }
   }
   // -D of the lane's row in every element: the initial accumulator of each
   // dP^T chain, so the products leave dP - D in place.
@@ -1075,6 +1130,14 @@ __global__ __launch_bounds__((64 * DqTile<D, MODE != 0>::NW), (MODE != 0 ? 2 : 1
   store_rows_staged<D>(st, lane, pq, make_rsrc(dQ + qoff, (uint32_t)Lq * D * 2), qw0);
 }
 
+// Whether the dQ kernel takes over the prepare kernel's work (a call that
+// runs both stages, with bf16 O): it then runs first and writes the
+// statistics that the dK/dV kernel, if requested, reads after it.
+inline bool fused_prepare(const BwdArgs& a, unsigned stages) {
+  constexpr unsigned both = kBwdPrepare | kBwdDq;
+  return (stages & both) == both && !a.o_f32 && a.BH > 0 && a.Lq > 0 && a.Lk > 0;
+}
+
 template <int D, bool CAUSAL, int QMODE>
 void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   constexpr bool SPARSE = QMODE == 2;
@@ -1085,24 +1148,30 @@ void launch_main(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const uint16_t* K = static_cast<const uint16_t*>(a.K);
   const uint16_t* V = static_cast<const uint16_t*>(a.V);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
+  const uint16_t* O = static_cast<const uint16_t*>(a.O);
   const int n_kt = (a.Lk + TK::BK - 1) / TK::BK;
+  const int n_qt = (a.Lq + TQ::BR - 1) / TQ::BR;
+  const bool fused = fused_prepare(a, stages);
+  auto dq = [&](auto PREPc) {
+    constexpr bool PREP = decltype(PREPc)::value;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QMODE, PREP>), dim3((unsigned)(n_qt * a.BH)),
+                       dim3(64 * TQ::NW), 0, stream, Q, K, V, dO, O, a.lse, a.lse2, a.Dvec,
+                       static_cast<uint16_t*>(a.dQ), a.BH, a.Lq, a.Lk, n_qt, c, a.scale,
+                       a.block_mask, a.bm_stride, a.nqb, a.nkb);
+  };
+  if (fused) dq(std::true_type{});
   if ((stages & kBwdDkDv) && n_kt > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)(n_kt * a.BH)),
                        dim3(64 * TK::NW), 0, stream, Q, K, V, dO, a.lse2, a.Dvec,
                        static_cast<uint16_t*>(a.dK), static_cast<uint16_t*>(a.dV), a.BH, a.Lq, a.Lk,
                        c, a.scale, a.block_mask, a.bm_stride, a.nqb, a.nkb);
-  const int n_qt = (a.Lq + TQ::BR - 1) / TQ::BR;
-  if ((stages & kBwdDq) && n_qt > 0 && a.Lk > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, QMODE>), dim3((unsigned)(n_qt * a.BH)),
-                       dim3(64 * TQ::NW), 0, stream, Q, K, V, dO, a.lse2, a.Dvec,
-                       static_cast<uint16_t*>(a.dQ), a.BH, a.Lq, a.Lk, n_qt, c, a.scale,
-                       a.block_mask, a.bm_stride, a.nqb, a.nkb);
+  if (!fused && (stages & kBwdDq) && n_qt > 0 && a.Lk > 0) dq(std::false_type{});
 }
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const int64_t rows = (int64_t)a.BH * a.Lq;
-  if ((stages & kBwdPrepare) && rows > 0) {
+  if ((stages & kBwdPrepare) && rows > 0 && !fused_prepare(a, stages)) {
     // The NT variant once bf16 O and dO together reach 64 MiB (with fp32 O
     // it measured no faster).
     const bool nt = !a.o_f32 && rows * D * 4 >= (int64_t(64) << 20);

@@ -52,7 +52,9 @@ struct BwdArgs {
 // Backward stages, run in this order by the launchers for the stages set in
 // `stages`: per-row statistics (D, and lse in base 2 for bf16) into the
 // workspace, then dK/dV, then dQ.  The last two only read the statistics
-// and are independent of each other.
+// and are independent of each other.  The bf16 launcher runs the first and
+// the last in one kernel when both are requested (and O is bf16), before
+// dK/dV.
 enum : unsigned { kBwdPrepare = 1u, kBwdDkDv = 2u, kBwdDq = 4u, kBwdAll = 7u };
 
 // Key-split forward (short query blocks, long key sequences).  Split s

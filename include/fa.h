@@ -147,7 +147,8 @@ FA_API size_t fa_bwd_workspace_bytes(fa_dtype in_dtype, int64_t B, int64_t H,
  * works"); the gradients are the chain rule through the forward:
  * dV = P^T dO, dS = P * (dO V^T - D), dK = scale dS^T Q, dQ = scale dS K.
  * Equivalent to fa_bwd_prepare, then fa_bwd_dkdv and fa_bwd_dq on the same
- * stream.  No atomics: every gradient row is summed in a fixed order by one
+ * stream, and to fa_bwd_prepare_dq then fa_bwd_dkdv (bit for bit, either
+ * way).  No atomics: every gradient row is summed in a fixed order by one
  * workgroup, so results are bitwise reproducible.
  *   in_dtype   dtype of Q, K, V, dO, dQ, dK, dV.
  *   o_dtype    dtype of O, as the forward wrote it: equal to in_dtype, or
@@ -216,6 +217,25 @@ FA_API fa_status fa_bwd_dq(fa_dtype in_dtype,
                  float scale, int causal,
                  void* dQ,
                  const void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * fa_bwd_prepare_dq is fa_bwd_prepare and fa_bwd_dq in one call: it writes
+ * the per-row statistics into `workspace` and dQ.  With bf16 O both run in
+ * one kernel (the dQ kernel forms D and lse in base 2 from the O, dO and
+ * lse rows it reads anyway, with the prepare stage's arithmetic in the
+ * same order, so the workspace and dQ get the same bits as the two stages
+ * give); with fp32 O, or fp32 inputs, the two stages run one after the
+ * other.  fa_bwd_dkdv can follow it on the same stream (this is what
+ * fa_bwd does).  Arguments as for fa_bwd.
+ */
+FA_API fa_status fa_bwd_prepare_dq(fa_dtype in_dtype, fa_dtype o_dtype,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 const void* Q, const void* K, const void* V,
+                 const void* O, const void* dO, const float* lse,
+                 float scale, int causal,
+                 void* dQ,
+                 void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
 /*

@@ -94,6 +94,18 @@ long long call(const std::string& fn, Args& a) {
     void *dQ = a.P(), *dK = a.P(), *dV = a.P();
     return fa_bwd_noalloc(it, ot, B, H, Lq, Lk, d, Q, K, V, O, G, L, sc, ca, dQ, dK, dV, a.S());
   }
+  if (fn == "fa_bwd_prepare_dq") {
+    fa_dtype it = a.D(), ot = a.D();
+    long long B = a.I(), H = a.I(), Lq = a.I(), Lk = a.I(), d = a.I();
+    void *Q = a.P(), *K = a.P(), *V = a.P(), *O = a.P(), *G = a.P();
+    const float* L = (const float*)a.P();
+    float sc = a.F();
+    int ca = (int)a.I();
+    void* dQ = a.P();
+    void* ws = a.P();
+    size_t wb = (size_t)a.I();
+    return fa_bwd_prepare_dq(it, ot, B, H, Lq, Lk, d, Q, K, V, O, G, L, sc, ca, dQ, ws, wb, a.S());
+  }
   if (fn == "fa_bwd_prepare") {
     fa_dtype it = a.D(), ot = a.D();
     long long B = a.I(), H = a.I(), Lq = a.I(), Lk = a.I(), d = a.I();

@@ -128,6 +128,9 @@ def _stage(lib, name, in_dt=BF16, o_dt=None, B=1, H=2, Lq=64, Lk=64, d=128, ptrs
     if name == "dkdv":
         return lib.fa_bwd_dkdv(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["dO"], scale,
                                causal, p["dK"], p["dV"], ws, ws_bytes, None)
+    if name == "prepare_dq":
+        return lib.fa_bwd_prepare_dq(in_dt, o_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["O"],
+                                     p["dO"], p["lse"], scale, causal, p["dQ"], ws, ws_bytes, None)
     return lib.fa_bwd_dq(in_dt, B, H, Lq, Lk, d, p["Q"], p["K"], p["V"], p["dO"], scale, causal,
                          p["dQ"], ws, ws_bytes, None)
 
@@ -144,6 +147,15 @@ def _stage(lib, name, in_dt=BF16, o_dt=None, B=1, H=2, Lq=64, Lk=64, d=128, ptrs
     ("dq", dict(ptrs=dict(dQ=None)), NULL), ("dq", dict(ptrs=dict(V=None)), NULL),
     ("dq", dict(ptrs=dict(dO=None)), NULL), ("dq", dict(ptrs=dict(Q=P + 4)), ALIGN),
     ("dq", dict(ws_bytes=0), WS), ("dq", dict(d=96), UNSUP),
+    # Both stages' checks: O, lse and O's dtype (prepare), K, V and dQ (dQ).
+    ("prepare_dq", dict(in_dt=4), ARG), ("prepare_dq", dict(o_dt=7), ARG),
+    ("prepare_dq", dict(in_dt=F32, o_dt=BF16), UNSUP), ("prepare_dq", dict(scale=float("inf")), ARG),
+    ("prepare_dq", dict(Lk=0), SHAPE), ("prepare_dq", dict(d=32), UNSUP),
+    ("prepare_dq", dict(ptrs=dict(O=None)), NULL), ("prepare_dq", dict(ptrs=dict(lse=None)), NULL),
+    ("prepare_dq", dict(ptrs=dict(dQ=None)), NULL), ("prepare_dq", dict(ptrs=dict(K=None)), NULL),
+    ("prepare_dq", dict(ptrs=dict(V=None)), NULL), ("prepare_dq", dict(ptrs=dict(O=P + 2)), ALIGN),
+    ("prepare_dq", dict(ptrs=dict(dQ=P + 8)), ALIGN), ("prepare_dq", dict(ws=None), WS),
+    ("prepare_dq", dict(ws_bytes=64), WS),
 ])
 def test_bwd_stages_reject(lib, name, kw, status):
     assert _stage(lib, name, **kw) == status
@@ -157,11 +169,12 @@ def test_bwd_stages_ignore_pointers_they_do_not_use(lib):
     assert _stage(lib, "prepare", ptrs=nul, ws=None) == WS
     assert _stage(lib, "dkdv", ptrs=dict(O=None, lse=None, dQ=None), ws=None) == WS
     assert _stage(lib, "dq", ptrs=dict(O=None, lse=None, dK=None, dV=None), ws=None) == WS
+    assert _stage(lib, "prepare_dq", ptrs=dict(dK=None, dV=None), ws=None) == WS
 
 
 def test_bwd_stages_empty_is_ok(lib):
     nul = {k: None for k in ("Q", "K", "V", "O", "dO", "lse", "dQ", "dK", "dV")}
-    for name in ("prepare", "dkdv", "dq"):
+    for name in ("prepare", "dkdv", "dq", "prepare_dq"):
         assert _stage(lib, name, B=0, ptrs=nul, ws=None, ws_bytes=0) == OK
 
 

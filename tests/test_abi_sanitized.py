@@ -97,6 +97,10 @@ VALID = [
     ("fa_bwd_prepare", (1, 0, 1, 2, 300, 300, 128, P, P, P, P, 1 << 20, None), OK),
     ("fa_bwd_dkdv", (1, 1, 2, 300, 300, 128, P, P, P, P, 0.1, 1, P, P, P, 1 << 20, None), OK),
     ("fa_bwd_dq", (1, 1, 2, 300, 300, 128, P, P, P, P, 0.1, 1, P, P, 1 << 20, None), OK),
+    ("fa_bwd_prepare_dq", (1, 1, 1, 2, 300, 300, 128, P, P, P, P, P, P, 0.1, 1, P, P, 1 << 20, None),
+     OK),
+    ("fa_bwd_prepare_dq", (1, 0, 1, 2, 300, 300, 64, P, P, P, P, P, P, 0.1, 0, P, P, 1 << 20, None),
+     OK),
     # Sizes at the edges of int64 and of the 32-bit per-slice offsets.
     ("fa_fwd", (1, 1, BIG, BIG, BIG, BIG, 128, P, P, P, 0.1, 1, P, P, None), SHAPE),
     ("fa_fwd", (1, 1, -BIG - 1, 1, 1, 1, 128, P, P, P, 0.1, 1, P, P, None), SHAPE),

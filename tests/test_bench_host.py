@@ -42,10 +42,9 @@ def test_kernel_table_bytes_and_flops(bench):
     assert kt["fwd_bf16_kernel"]["bytes"] == 4 * t + r == 134_742_016
     # dK/dV: Q, K, V, dO, lse2, D in; dK, dV out
     assert kt["bwd_dkdv_kernel"]["bytes"] == 6 * t + 2 * r == 202_375_168
-    # dQ: Q, K, V, dO, lse2, D in; dQ out
-    assert kt["bwd_dq_kernel"]["bytes"] == 5 * t + 2 * r
-    # pre: O, dO, lse in; D, lse2 out
-    assert kt["bwd_pre_bf16_kernel"]["bytes"] == 2 * t + 3 * r
+    # dQ with the row statistics: Q, K, V, dO, O, lse in; D, lse2 and dQ out
+    assert kt["bwd_dq_kernel"]["bytes"] == 6 * t + 3 * r
+    assert set(kt) == {"fwd_bf16_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"}
     f1 = 2 * d * (L * L // 2) * B * H  # one product over the visible pairs
     assert kt["fwd_bf16_kernel"]["flops"] == 2 * f1
     assert kt["bwd_dkdv_kernel"]["flops"] == 4 * f1

@@ -143,6 +143,37 @@ def test_stages_equal_fused_call_across_two_streams(dtype):
     assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
 
 
+@pytest.mark.parametrize("dtype,o32", [("bf16", False), ("bf16", True), ("f32", False)],
+                         ids=["bf16", "bf16-fp32O", "f32"])
+@pytest.mark.parametrize("shape,causal", [((1, 3, 333, 333, 128), True), ((2, 2, 200, 517, 64), False),
+                                          ((1, 2, 517, 300, 64), True)],
+                         ids=["B1H3L333d128c", "B2H2Lq200Lk517d64n", "B1H2Lq517Lk300d64c"])
+def test_prepare_dq_then_dkdv_equals_fa_bwd(dtype, o32, shape, causal):
+    # fa_bwd_prepare_dq (one kernel when O is bf16) then fa_bwd_dkdv give
+    # fa_bwd's bits, and the statistics it leaves in the workspace are
+    # fa_bwd_prepare's bit for bit.
+    B, H, Lq, Lk, d = shape
+    q, k, v, do = make_inputs(B, H, Lq, Lk, d, dtype, seed=7 * Lq + d, with_dO=True)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    announce(f"bwd prepare_dq {dtype} fp32O={o32} {shape} causal={causal}")
+    kw = dict(out_dtype=torch.float32) if o32 else {}
+    O, lse = fa.fa_fwd(qd, kd, vd, causal=causal, **kw)
+    ref = fa.fa_bwd(qd, kd, vd, O, dod, lse, causal=causal)
+    nbytes = fa.fa_bwd_workspace_bytes(qd.dtype, B, H, Lq, Lk, d)
+    ws1 = torch.zeros(nbytes, dtype=torch.uint8, device=qd.device)
+    ws2 = torch.zeros(nbytes, dtype=torch.uint8, device=qd.device)
+    dq = fa.fa_bwd_prepare_dq(qd, kd, vd, O, dod, lse, ws1, causal=causal)
+    dk, dv = fa.fa_bwd_dkdv(qd, kd, vd, dod, ws1, causal=causal)
+    fa.fa_bwd_prepare(O, dod, lse, Lk, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(ws1, ws2)
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+    got = (f64(dq), f64(dk), f64(dv))
+    want = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), 1 / math.sqrt(d), causal)
+    _assert_grads(got, want, BF16_GRAD_REL if dtype == "bf16" else F32_REL,
+                  f"prepare_dq {dtype} {shape}")
+
+
 def _gpu_grads_f32_out(q, k, v, do, scale, causal):
     # The forward's fp32-output variant, whose O goes into the backward as
     # fp32 (o_dtype = FA_F32); dO stays bf16.
