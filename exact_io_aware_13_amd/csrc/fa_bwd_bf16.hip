@@ -8,10 +8,13 @@
 // chain rule through the forward: dV = P^T dO, dP = dO V^T,
 // dS = P * (dP - D), dK = scale dS^T Q, dQ = scale dS K.
 //
-// Three kernels, no atomics, every output written once by one workgroup in
+// Three stages, no atomics, every output written once by one workgroup in
 // a fixed summation order (so the backward is bitwise deterministic):
 //  1. pre:   -D_i = -rowsum(dO * O) and lse in base 2, per query row (the
-//            negated D starts the dK/dV kernel's dP accumulation).
+//            negated D starts the dP accumulations).  When a call runs it
+//            together with dQ (fa_bwd does) and O is bf16, the dQ kernel
+//            does this work for its own rows and runs first, so the
+//            separate kernel and its second read of dO drop out.
 //  2. dK/dV: key-stationary.  One workgroup = 4 waves = 128 keys of one
 //            slice (32 per wave); K and V rows stay in registers as
 //            matrix-product operands, dK and dV accumulate in registers
