@@ -20,7 +20,8 @@
 // LDS in a fixed order (the softmax merge of the running statistics for the
 // forward, plain sums for the gradients), so results are bitwise
 // reproducible.  Short sequences thus run on four times as many waves, which
-// is what bounds the latency of the smallest workloads.
+// is what bounds the latency of the smallest workloads (the forward at
+// d = 64 takes eight waves when its grid is smaller than the chip).
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -73,9 +74,10 @@ __device__ __forceinline__ void store_cols(float* p, const float (&v)[kCols], fl
   }
 }
 
-// The contiguous part [lo, hi) of [0, n) that wave w of kWaves takes.
+// The contiguous part [lo, hi) of [0, n) that wave w of NWV takes.
+template <int NWV = kWaves>
 __device__ __forceinline__ void wave_part(int n, int w, int& lo, int& hi) {
-  const int chunk = (n + kWaves - 1) / kWaves;
+  const int chunk = (n + NWV - 1) / NWV;
   lo = min(n, w * chunk);
   hi = min(n, lo + chunk);
 }
@@ -101,18 +103,21 @@ struct F32Ring {
   static_assert(LPC >= 1 && LPC * RPI == CH, "chunk split");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
+// NWV waves per workgroup: kWaves, or twice that at d = 64 for launches of
+// fewer workgroups than compute units, where each wave's chain of key
+// chunks sets the latency (half the keys per wave, half the chain).
+template <int D, bool CAUSAL, int NWV>
+__global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Lq, int Lk, float c) {
   using T = F32Tile<D>;
   using RG = F32Ring<D>;
   // One array per ring slot (every wave's part of it), selected at compile
   // time, so the compiler relates each LDS read only to its own slot's loads.
-  __shared__ __attribute__((aligned(1024))) char R0[kWaves * RG::SLOTB];
-  __shared__ __attribute__((aligned(1024))) char R1[kWaves * RG::SLOTB];
-  __shared__ __attribute__((aligned(1024))) char R2[kWaves * RG::SLOTB];
-  __shared__ __attribute__((aligned(1024))) char R3[kWaves * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R0[NWV * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R1[NWV * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R2[NWV * RG::SLOTB];
+  __shared__ __attribute__((aligned(1024))) char R3[NWV * RG::SLOTB];
   auto rslot = [&](auto I) __attribute__((always_inline)) -> char* {
     constexpr int v = decltype(I)::value;
     if constexpr (v == 0) return R0;
@@ -121,8 +126,8 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
     else return R3;
   };
   static_assert(kRing == 4, "four slot arrays");
-  __shared__ float sm[kWaves][T::RPW], sl[kWaves][T::RPW];
-  __shared__ float sacc[kWaves][64][kCols + 1];
+  __shared__ float sm[NWV][T::RPW], sl[NWV][T::RPW];
+  __shared__ float sacc[NWV][64][kCols + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
   // Keys any row of the workgroup sees, split over the waves.
   const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
   int k_lo, k_hi;
-  wave_part(kend, w, k_lo, k_hi);
+  wave_part<NWV>(kend, w, k_lo, k_hi);
   const int nch = (k_hi - k_lo + RG::CH - 1) / RG::CH;
 
   // Chunk ch of the part into its slot: lane l of load i moves the 16 bytes
@@ -238,12 +243,12 @@ __global__ __launch_bounds__(64 * kWaves) void fwd_f32_kernel(
   if (w == 0) {
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm[ww][r]);
+    for (int ww = 0; ww < NWV; ++ww) M = fmaxf(M, sm[ww][r]);
     float lt = 0.f, o[kCols];
 #pragma unroll
     for (int i = 0; i < kCols; ++i) o[i] = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NWV; ++ww) {
       const float mw = sm[ww][r];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
       lt = fmaf(sl[ww][r], f, lt);
@@ -556,10 +561,23 @@ template <int D, bool CAUSAL>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream) {
   using T = F32Tile<D>;
   const int n_qt = (a.Lq + T::RPW - 1) / T::RPW;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)), dim3(64 * kWaves),
-                     0, stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
-                     static_cast<const float*>(a.V), static_cast<float*>(a.O), a.lse, a.BH, a.Lq,
-                     a.Lk, a.scale * kLog2e);
+  const int64_t wgs = (int64_t)n_qt * a.BH;
+  auto go = [&](auto NWc) {
+    constexpr int NWV = decltype(NWc)::value;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, NWV>), dim3((unsigned)wgs), dim3(64 * NWV), 0,
+                       stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+                       static_cast<const float*>(a.V), static_cast<float*>(a.O), a.lse, a.BH, a.Lq,
+                       a.Lk, a.scale * kLog2e);
+  };
+  // Eight waves' rings and merge buffers fit a compute unit's LDS at d = 64
+  // (99 KiB; 163 KiB at d = 128, more than there is).
+  if constexpr (D == 64) {
+    if (wgs < kComputeUnits) {
+      go(IC<2 * kWaves>{});
+      return hipGetLastError();
+    }
+  }
+  go(IC<kWaves>{});
   return hipGetLastError();
 }
 

@@ -30,8 +30,13 @@ def test_fp32_kernels_do_not_spill(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     meta = out.read_text()
     names = re.findall(r"\.name:\s+(\S+_f32_kernel\S*)", meta)
-    assert len(names) == 14, names          # fwd, pre, dK/dV, dQ over d and the causal flag
+    # fwd, pre, dK/dV, dQ over d and the causal flag, plus the eight-wave
+    # forward at d = 64 (both masks)
+    assert len(names) == 16, names
     spills = [int(x) for x in re.findall(r"\.vgpr_spill_count:\s+(\d+)", meta)]
     scratch = [int(x) for x in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", meta)]
     assert spills and max(spills) == 0, spills
     assert scratch and max(scratch) == 0, scratch
+    # Every workgroup's LDS fits a compute unit (160 KiB).
+    lds = [int(x) for x in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", meta)]
+    assert len(lds) == len(names) and max(lds) <= 160 * 1024, lds
