@@ -43,6 +43,14 @@ fa_status check_shape(fa_dtype in_dtype, int64_t B, int64_t H, int64_t Lq, int64
   // Grid sizes (x dimension) of the largest launch, query- or key-side, must fit.
   if (bh * cdiv(Lq, rows_per_block) > INT32_MAX || bh * cdiv(Lk, rows_per_block) > INT32_MAX)
     return FA_ERR_SHAPE;
+  // So must its work-item count (grid x workgroup size), which a dispatch
+  // carries in 32 bits: at most D/8 threads per query row (the bf16 prepare
+  // kernel; every other bf16 kernel uses 2-4) and 32 per row or key at fp32,
+  // over the rows padded to a whole workgroup.  Only sizes near the device
+  // memory (2^28 bf16 rows of d = 128) reach it.
+  const int64_t threads_per_row = in_dtype == FA_BF16 ? d / 8 : 32;
+  const int64_t longest = std::max(Lq, Lk) + 256;
+  if (bh * longest * threads_per_row > int64_t(UINT32_MAX)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -56,7 +64,7 @@ const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or too large sizes (negative size, Lk = 0 with Lq > 0, or over 2^31 bytes per slice)";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or too large sizes (negative size, Lk = 0 with Lq > 0, over 2^31 bytes per slice, or over 2^32 threads in one launch)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension or dtype combination not implemented (d must be 64 or 128)";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL or smaller than the matching *_workspace_bytes() size";

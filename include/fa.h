@@ -65,7 +65,10 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   FA_ERR_SHAPE = 2,       /* negative size, Lk = 0 with Lq > 0, or a size too
-                             large for 32-bit per-slice offsets                 */
+                             large for 32-bit per-slice offsets or for a
+                             launch's 32-bit work-item count (B*H times the
+                             longer length, times d/8 at bf16 or 32 at fp32,
+                             over 2^32)                                         */
   FA_ERR_UNSUPPORTED = 3, /* valid request the kernels do not implement (head
                              dimension, dtype combination)                     */
   FA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned             */

@@ -183,6 +183,21 @@ def test_bwd_empty_is_ok(lib):
     assert _bwd(lib, B=0, ptrs=nul, ws=None, ws_bytes=0) == OK
 
 
+def test_launch_work_items_fit_32_bits(lib):
+    # A dispatch carries its work-item count (grid x workgroup size) in 32
+    # bits: sizes whose largest launch would exceed it are rejected, sizes
+    # just below are accepted (the workspace helper validates like fa_bwd
+    # and returns 0 for what fa_bwd rejects).
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 65536, 4096, 4096, 128) == 0
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 60000, 4096, 4096, 128) > 0
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 131072, 4096, 4096, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(BF16, 1, 120000, 4096, 4096, 64) > 0
+    assert lib.fa_bwd_workspace_bytes(F32, 1, 32768, 4096, 4096, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(F32, 1, 30000, 4096, 4096, 64) > 0
+    assert _fwd(lib, B=1, H=65536, Lq=4096, Lk=4096) == SHAPE
+    assert _fwd(lib, B=2, H=32768, Lq=4096, Lk=4096, in_dt=F32, out_dt=F32, d=64) == SHAPE
+
+
 def test_workspace_is_linear_in_length(lib):
     mem = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_example_memory.json")))
     L, L2 = mem["L"], mem["L_doubled"]
