@@ -443,14 +443,14 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
   // register set is current; FIRST (j = 0) has no previous value product.
   auto iter = [&](auto Rc, auto FIRSTc, int j, f32x16 (&s_cur)[T::RB][T::NKB],
                   f32x16 (&s_next)[T::RB][T::NKB], const unsigned (&pk_prev)[T::RB][T::NKB][8],
-                  unsigned (&pk_cur)[T::RB][T::NKB][8]) __attribute__((always_inline)) {
+                  unsigned (&pk_cur)[T::RB][T::NKB][8], u32x4 (&pre)[4]) __attribute__((always_inline)) {
     constexpr int R = decltype(Rc)::value;
     constexpr bool FIRST = decltype(FIRSTc)::value;
     const char* kb = kslot(IC<(R + 1) % 4>{}) + gofs;  // K[j+1]
     const char* vb = vslot(IC<(R + 3) % 4>{}) + gofs;  // V[j-1]
 
     // K[j+1] and V[j-1] were fetched three iterations ahead and waited for
-    // at the end of iteration j-1.  This iteration refills the slots of K[j]
+    // at the end of iteration j-2.  This iteration refills the slots of K[j]
     // and V[j-2], whose last readers ran in iteration j-1 (closed by its
     // barrier), with K[j+4] and V[j+2], from inside the product sequence.
 
@@ -532,11 +532,15 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
     // NFRAG steps: score products of K fragment i (every row block), value
     // products of V fragment i (every row block), slot work after each.
     u32x4 ka[T::NFRAG], va[T::NFRAG];
-    ka[0] = kread(kb, 0);
-    ka[1] = kread(kb, 1);
-    if constexpr (!FIRST) {
-      va[0] = vread(vb, 0);
-      va[1] = vread(vb, 1);
+    if constexpr (FIRST) {
+      ka[0] = kread(kb, 0);
+      ka[1] = kread(kb, 1);
+    } else {
+      // Read during iteration j-1 (see the end of the product sequence).
+      ka[0] = pre[0];
+      ka[1] = pre[1];
+      va[0] = pre[2];
+      va[1] = pre[3];
     }
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, T::NFRAG>([&](auto Ic) __attribute__((always_inline)) {
@@ -551,6 +555,14 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
       if constexpr (i + 2 < T::NFRAG) {
         ka[i + 2] = kread(kb, i + 2);
         if constexpr (!FIRST) va[i + 2] = vread(vb, i + 2);
+      } else {
+        // The next iteration's first K and V fragments: K[j+2] and V[j]
+        // were waited for at the end of iteration j-1 and made visible by
+        // its barrier, so they are read now and the next iteration starts
+        // its products right after its barrier.
+        constexpr int f = i + 2 - T::NFRAG;
+        pre[f] = kread(kslot(IC<(R + 2) % 4>{}) + gofs, f);
+        pre[2 + f] = vread(vslot(IC<R>{}) + gofs, f);
       }
       static_for<0, T::RB>([&](auto RBc) __attribute__((always_inline)) {
         constexpr int rb = decltype(RBc)::value;
@@ -627,7 +639,9 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
     }
 #pragma unroll
     for (int rb = 0; rb < T::RB; ++rb) l[rb] += tsum[rb];
-    wait_vm<4 * T::LOADS>();  // loads of iteration j-2 and older landed
+    // Loads of iteration j-1 and older landed (K[j+3], V[j+1], which the
+    // end of iteration j+1 reads).
+    wait_vm<2 * T::LOADS>();
     block_barrier();
   };
 
@@ -649,23 +663,24 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
   fetch(rk, 3, K3);
   __builtin_amdgcn_sched_barrier(0);
   fetch(rv, 1, V1);
-  wait_vm<4 * T::LOADS>();  // K0 and K1 landed
+  wait_vm<2 * T::LOADS>();  // K0, K1, K2 and V0 landed
   block_barrier();
   score_tile(K0 + gofs, sA);
   block_barrier();  // every wave is done with K0 before iteration 0 refills its slot
 
-  iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB);
+  u32x4 pre[4];
+  iter(IC<0>{}, std::true_type{}, 0, sA, sB, pA, pB, pre);
   // Four iterations per trip (j = 1..4 mod 4) as one straight-line chain, so
   // ring slots and register roles are compile-time in every body.
   for (int j = 1; j < nkt_w; j += 4) {
     window_for(min(j + 7, nkt - 1));  // this trip fetches up to tile j + 7
-    iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA);
+    iter(IC<1>{}, std::false_type{}, j, sB, sA, pB, pA, pre);
     if (j + 1 >= nkt_w) break;
-    iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB);
+    iter(IC<2>{}, std::false_type{}, j + 1, sA, sB, pA, pB, pre);
     if (j + 2 >= nkt_w) break;
-    iter(IC<3>{}, std::false_type{}, j + 2, sB, sA, pB, pA);
+    iter(IC<3>{}, std::false_type{}, j + 2, sB, sA, pB, pA, pre);
     if (j + 3 >= nkt_w) break;
-    iter(IC<0>{}, std::false_type{}, j + 3, sA, sB, pA, pB);
+    iter(IC<0>{}, std::false_type{}, j + 3, sA, sB, pA, pB, pre);
   }
 
   // Value product of the wave's last tile: P(nkt_w-1) is in pB when nkt_w-1
@@ -696,7 +711,7 @@ __global__ __launch_bounds__((64 * FwdTile<D, MODE != 0>::NW * (MODE == 3 ? 2 : 
       char* vs = (j & 3) == 0 ? V2 : (j & 3) == 1 ? V3 : (j & 3) == 2 ? V0 : V1;
       fetch(rk, j + 4, ks);
       fetch(rv, j + 2, vs);
-      wait_vm<4 * T::LOADS>();
+      wait_vm<2 * T::LOADS>();
       block_barrier();
     }
     wait_vm<0>();
