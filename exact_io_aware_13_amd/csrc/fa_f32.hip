@@ -34,11 +34,11 @@ constexpr int kWaves = 4;        // waves per workgroup (they split the streamed
 constexpr int kCols = 16;        // columns of a row per lane
 constexpr int kGroup = 4;        // streamed rows per inner step
 
-template <int D>
+template <int D, int COLS = kCols>
 struct F32Tile {
-  static constexpr int LPR = D / kCols;        // lanes per row
+  static constexpr int LPR = D / COLS;         // lanes per row
   static constexpr int RPW = 64 / LPR;         // rows per wave (= per workgroup)
-  static_assert(kCols * LPR == D, "head dimension split");
+  static_assert(COLS * LPR == D && COLS % 4 == 0, "head dimension split");
 };
 
 // Sum over the LPR consecutive lanes that hold one row.
@@ -49,10 +49,11 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ void load_cols(const float* p, float (&v)[kCols]) {
+template <int N>
+__device__ __forceinline__ void load_cols(const float* p, float (&v)[N]) {
   const f32x4* q = reinterpret_cast<const f32x4*>(p);
 #pragma unroll
-  for (int i = 0; i < kCols / 4; ++i) {
+  for (int i = 0; i < N / 4; ++i) {
     const f32x4 x = q[i];
     v[4 * i] = x[0];
     v[4 * i + 1] = x[1];
@@ -61,10 +62,11 @@ __device__ __forceinline__ void load_cols(const float* p, float (&v)[kCols]) {
   }
 }
 
-__device__ __forceinline__ void store_cols(float* p, const float (&v)[kCols], float s) {
+template <int N>
+__device__ __forceinline__ void store_cols(float* p, const float (&v)[N], float s) {
   f32x4* q = reinterpret_cast<f32x4*>(p);
 #pragma unroll
-  for (int i = 0; i < kCols / 4; ++i) {
+  for (int i = 0; i < N / 4; ++i) {
     f32x4 x;
     x[0] = v[4 * i] * s;
     x[1] = v[4 * i + 1] * s;
@@ -106,11 +108,11 @@ struct F32Ring {
 // NWV waves per workgroup: kWaves, or twice that at d = 64 for launches of
 // fewer workgroups than compute units, where each wave's chain of key
 // chunks sets the latency (half the keys per wave, half the chain).
-template <int D, bool CAUSAL, int NWV>
+template <int D, bool CAUSAL, int NWV, int COLS>
 __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int Lq, int Lk, float c) {
-  using T = F32Tile<D>;
+  using T = F32Tile<D, COLS>;
   using RG = F32Ring<D>;
   // One array per ring slot (every wave's part of it), selected at compile
   // time, so the compiler relates each LDS read only to its own slot's loads.
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
   };
   static_assert(kRing == 4, "four slot arrays");
   __shared__ float sm[NWV][T::RPW], sl[NWV][T::RPW];
-  __shared__ float sacc[NWV][64][kCols + 1];
+  __shared__ float sacc[NWV][64][COLS + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
@@ -139,10 +141,10 @@ __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
   const auto rk = make_rsrc(K + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
   const auto rv = make_rsrc(V + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
 
-  float q[kCols], acc[kCols];
-  load_cols(Q + qrow * D + cc * kCols, q);
+  float q[COLS], acc[COLS];
+  load_cols(Q + qrow * D + cc * COLS, q);
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+  for (int i = 0; i < COLS; ++i) acc[i] = 0.f;
   // Keys any row of the workgroup sees, split over the waves.
   const int kend = CAUSAL ? min(Lk, r0 + T::RPW) : Lk;
   int k_lo, k_hi;
@@ -182,18 +184,18 @@ __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
     const float* kb = reinterpret_cast<const float*>(rslot(Sc) + w * RG::SLOTB);
     const float* vb = kb + RG::CHB / 4;
     const int j0 = k_lo + ch * RG::CH;
-    float kv[kGroup][kCols], vv[kGroup][kCols], t[kGroup];
+    float kv[kGroup][COLS], vv[kGroup][COLS], t[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      load_cols(kb + g * D + cc * kCols, kv[g]);
-      load_cols(vb + g * D + cc * kCols, vv[g]);
+      load_cols(kb + g * D + cc * COLS, kv[g]);
+      load_cols(vb + g * D + cc * COLS, vv[g]);
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < kCols; ++i) dot = fmaf(q[i], kv[g][i], dot);
+      for (int i = 0; i < COLS; ++i) dot = fmaf(q[i], kv[g][i], dot);
       dot = row_sum<T::LPR>(dot);
       const int j = j0 + g;
       t[g] = (j < k_hi && !(CAUSAL && j > qi)) ? dot * c : -INFINITY;
@@ -207,13 +209,13 @@ __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int i = 0; i < kCols; ++i) acc[i] *= alpha;
+    for (int i = 0; i < COLS; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       const float p = exp2f(t[g] - base);
       l += p;
 #pragma unroll
-      for (int i = 0; i < kCols; ++i) acc[i] = fmaf(p, vv[g][i], acc[i]);
+      for (int i = 0; i < COLS; ++i) acc[i] = fmaf(p, vv[g][i], acc[i]);
     }
   };
   if (nch > 0) {
@@ -238,25 +240,25 @@ __global__ __launch_bounds__(64 * NWV) void fwd_f32_kernel(
     sl[w][r] = l;
   }
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) sacc[w][lane][i] = acc[i];
+  for (int i = 0; i < COLS; ++i) sacc[w][lane][i] = acc[i];
   __syncthreads();
   if (w == 0) {
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < NWV; ++ww) M = fmaxf(M, sm[ww][r]);
-    float lt = 0.f, o[kCols];
+    float lt = 0.f, o[COLS];
 #pragma unroll
-    for (int i = 0; i < kCols; ++i) o[i] = 0.f;
+    for (int i = 0; i < COLS; ++i) o[i] = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NWV; ++ww) {
       const float mw = sm[ww][r];
       const float f = mw == -INFINITY ? 0.f : exp2f(mw - M);
       lt = fmaf(sl[ww][r], f, lt);
 #pragma unroll
-      for (int i = 0; i < kCols; ++i) o[i] = fmaf(sacc[ww][lane][i], f, o[i]);
+      for (int i = 0; i < COLS; ++i) o[i] = fmaf(sacc[ww][lane][i], f, o[i]);
     }
     if (valid) {
-      store_cols(O + qrow * D + cc * kCols, o, 1.f / lt);
+      store_cols(O + qrow * D + cc * COLS, o, 1.f / lt);
       if (cc == 0) LSE[qrow] = (M + log2f(lt)) * kLn2;
     }
   }
@@ -559,25 +561,34 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
 
 template <int D, bool CAUSAL>
 hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream) {
-  using T = F32Tile<D>;
-  const int n_qt = (a.Lq + T::RPW - 1) / T::RPW;
-  const int64_t wgs = (int64_t)n_qt * a.BH;
-  auto go = [&](auto NWc) {
-    constexpr int NWV = decltype(NWc)::value;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, NWV>), dim3((unsigned)wgs), dim3(64 * NWV), 0,
-                       stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
+  auto go = [&](auto NWc, auto COLSc) {
+    constexpr int NWV = decltype(NWc)::value, COLS = decltype(COLSc)::value;
+    using T = F32Tile<D, COLS>;
+    const int64_t wgs = (int64_t)((a.Lq + T::RPW - 1) / T::RPW) * a.BH;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, NWV, COLS>), dim3((unsigned)wgs), dim3(64 * NWV),
+                       0, stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
                        static_cast<const float*>(a.V), static_cast<float*>(a.O), a.lse, a.BH, a.Lq,
                        a.Lk, a.scale * kLog2e);
   };
-  // Eight waves' rings and merge buffers fit a compute unit's LDS at d = 64
-  // (99 KiB; 163 KiB at d = 128, more than there is).
+  // At d = 64 a grid smaller than the chip takes eight waves per workgroup
+  // (their rings and merge buffers fit a compute unit's LDS; at d = 128
+  // they would not) and spreads each row over more lanes -- 4 or 8 columns
+  // each instead of 16, the fewest columns whose grid still fits the chip
+  // in one round -- so the same work runs on 2-4x the compute units
+  // (B1 H1 L128 d64: 7.8 -> 5.5 us; B1 H4 L512 d64: 18.8 -> 14.3 us).
   if constexpr (D == 64) {
-    if (wgs < kComputeUnits) {
-      go(IC<2 * kWaves>{});
+    auto wgs = [&](auto COLSc) {
+      using T = F32Tile<D, decltype(COLSc)::value>;
+      return (int64_t)((a.Lq + T::RPW - 1) / T::RPW) * a.BH;
+    };
+    if (wgs(IC<kCols>{}) < kComputeUnits) {
+      if (wgs(IC<4>{}) <= kComputeUnits) go(IC<2 * kWaves>{}, IC<4>{});
+      else if (wgs(IC<8>{}) <= kComputeUnits) go(IC<2 * kWaves>{}, IC<8>{});
+      else go(IC<2 * kWaves>{}, IC<kCols>{});
       return hipGetLastError();
     }
   }
-  go(IC<kWaves>{});
+  go(IC<kWaves>{}, IC<kCols>{});
   return hipGetLastError();
 }
 

@@ -66,7 +66,11 @@ def test_f32_workload():
         assert rel_to_max(f64(lse), lse_ref) <= F32_REL
 
 
-@pytest.mark.parametrize("shape", [(1, 2, 1, 1, 64), (2, 1, 65, 300, 128), (1, 3, 300, 300, 64)],
+# At d = 64 the launcher picks 4, 8 or 16 columns per lane by grid size:
+# (1, 3, 300, 300) takes 4, (1, 3, 601, 601) 8 (ragged), (1, 7, 512, 512) 16
+# with eight waves, (2, 1, 65, 300, 128) the four-wave d = 128 kernel.
+@pytest.mark.parametrize("shape", [(1, 2, 1, 1, 64), (2, 1, 65, 300, 128), (1, 3, 300, 300, 64),
+                                   (1, 3, 601, 601, 64), (1, 7, 512, 512, 64)],
                          ids=lambda s: "B{}H{}Lq{}Lk{}d{}".format(*s))
 @pytest.mark.parametrize("causal", [False, True])
 def test_f32_small_shapes(shape, causal):
