@@ -66,11 +66,13 @@ def test_f32_workload():
         assert rel_to_max(f64(lse), lse_ref) <= F32_REL
 
 
-# At d = 64 the launcher picks 4, 8 or 16 columns per lane by grid size:
+# The launcher picks 4, 8 or 16 columns per lane by grid size: at d = 64
 # (1, 3, 300, 300) takes 4, (1, 3, 601, 601) 8 (ragged), (1, 7, 512, 512) 16
-# with eight waves, (2, 1, 65, 300, 128) the four-wave d = 128 kernel.
+# with eight waves; at d = 128 (2, 1, 65, 300) takes 4, (1, 2, 300, 300) 8,
+# (1, 4, 512, 512) 16.
 @pytest.mark.parametrize("shape", [(1, 2, 1, 1, 64), (2, 1, 65, 300, 128), (1, 3, 300, 300, 64),
-                                   (1, 3, 601, 601, 64), (1, 7, 512, 512, 64)],
+                                   (1, 3, 601, 601, 64), (1, 7, 512, 512, 64),
+                                   (1, 2, 300, 300, 128), (1, 4, 512, 512, 128)],
                          ids=lambda s: "B{}H{}Lq{}Lk{}d{}".format(*s))
 @pytest.mark.parametrize("causal", [False, True])
 def test_f32_small_shapes(shape, causal):
