@@ -285,13 +285,13 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(const float* __restric
 // wave streams its query rows (Q, dO, and the rows' base-2 lse and D)
 // through a private LDS ring as the forward streams keys.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int COLS>
 __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     float* __restrict__ dK, float* __restrict__ dV, int BH, int Lq, int Lk, float c,
     float scale) {
-  using T = F32Tile<D>;
+  using T = F32Tile<D, COLS>;
   using RG = F32Ring<D>;
   constexpr int SB = RG::SLOTB + 32;  // Q rows, dO rows, 4 lse2, 4 D
   __shared__ __attribute__((aligned(1024))) char R0[kWaves * SB];
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     else if constexpr (v == 2) return R2;
     else return R3;
   };
-  __shared__ float sk[kWaves][64][kCols + 1], sv[kWaves][64][kCols + 1];
+  __shared__ float sk[kWaves][64][COLS + 1], sv[kWaves][64][COLS + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
@@ -314,11 +314,11 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
   const int kj = k0 + r;
   const bool valid = kj < Lk;
   const size_t krow = (size_t)bh * Lk + (valid ? kj : 0);
-  float kr[kCols], vr[kCols], ak[kCols], av[kCols];
-  load_cols(K + krow * D + cc * kCols, kr);
-  load_cols(V + krow * D + cc * kCols, vr);
+  float kr[COLS], vr[COLS], ak[COLS], av[COLS];
+  load_cols(K + krow * D + cc * COLS, kr);
+  load_cols(V + krow * D + cc * COLS, vr);
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) {
+  for (int i = 0; i < COLS; ++i) {
     ak[i] = 0.f;
     av[i] = 0.f;
   }
@@ -370,17 +370,17 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     const float* gb = qb + RG::CHB / 4;
     const float* st = reinterpret_cast<const float*>(slot + RG::SLOTB);
     const int i0 = q_lo + ch * RG::CH;
-    float qv[kGroup][kCols], gv[kGroup][kCols];
+    float qv[kGroup][COLS], gv[kGroup][COLS];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      load_cols(qb + g * D + cc * kCols, qv[g]);
-      load_cols(gb + g * D + cc * kCols, gv[g]);
+      load_cols(qb + g * D + cc * COLS, qv[g]);
+      load_cols(gb + g * D + cc * COLS, gv[g]);
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) {
+      for (int x = 0; x < COLS; ++x) {
         s = fmaf(qv[g][x], kr[x], s);
         dp = fmaf(gv[g][x], vr[x], dp);
       }
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
       const float p = vis ? exp2f(s * c - st[g]) : 0.f;
       const float ds = p * (dp - st[4 + g]);
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) {
+      for (int x = 0; x < COLS; ++x) {
         av[x] = fmaf(p, gv[g][x], av[x]);
         ak[x] = fmaf(ds, qv[g][x], ak[x]);
       }
@@ -414,27 +414,27 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
     wait_vm<0>();
   }
 #pragma unroll
-  for (int x = 0; x < kCols; ++x) {
+  for (int x = 0; x < COLS; ++x) {
     sk[w][lane][x] = ak[x];
     sv[w][lane][x] = av[x];
   }
   __syncthreads();
   if (w == 0 && valid) {
-    float tk[kCols], tv[kCols];
+    float tk[COLS], tv[COLS];
 #pragma unroll
-    for (int x = 0; x < kCols; ++x) {
+    for (int x = 0; x < COLS; ++x) {
       tk[x] = sk[0][lane][x];
       tv[x] = sv[0][lane][x];
     }
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww)
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) {
+      for (int x = 0; x < COLS; ++x) {
         tk[x] += sk[ww][lane][x];
         tv[x] += sv[ww][lane][x];
       }
-    store_cols(dK + krow * D + cc * kCols, tk, scale);
-    store_cols(dV + krow * D + cc * kCols, tv, 1.f);
+    store_cols(dK + krow * D + cc * COLS, tk, scale);
+    store_cols(dV + krow * D + cc * COLS, tv, 1.f);
   }
 }
 
@@ -443,12 +443,12 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dkdv_f32_kernel(
 // the four partial sums are added in wave order.  Keys stream through a
 // private LDS ring per wave, as in the forward.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int COLS>
 __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dvec,
     float* __restrict__ dQ, int BH, int Lq, int Lk, float c, float scale) {
-  using T = F32Tile<D>;
+  using T = F32Tile<D, COLS>;
   using RG = F32Ring<D>;
   __shared__ __attribute__((aligned(1024))) char R0[kWaves * RG::SLOTB];
   __shared__ __attribute__((aligned(1024))) char R1[kWaves * RG::SLOTB];
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     else if constexpr (v == 2) return R2;
     else return R3;
   };
-  __shared__ float sq[kWaves][64][kCols + 1];
+  __shared__ float sq[kWaves][64][COLS + 1];
   const int tid = wi_id();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r = lane / T::LPR, cc = lane % T::LPR;
@@ -470,11 +470,11 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
   const int qi = r0 + r;
   const bool valid = qi < Lq;
   const size_t qrow = (size_t)bh * Lq + (valid ? qi : 0);
-  float qr[kCols], gr[kCols], aq[kCols];
-  load_cols(Q + qrow * D + cc * kCols, qr);
-  load_cols(dO + qrow * D + cc * kCols, gr);
+  float qr[COLS], gr[COLS], aq[COLS];
+  load_cols(Q + qrow * D + cc * COLS, qr);
+  load_cols(dO + qrow * D + cc * COLS, gr);
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) aq[i] = 0.f;
+  for (int i = 0; i < COLS; ++i) aq[i] = 0.f;
   const float lse2 = LSE2[qrow];
   const float Di = Dvec[qrow];
   const auto rk = make_rsrc(K + (size_t)bh * Lk * D, (uint32_t)Lk * RG::ROWB);
@@ -506,17 +506,17 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     const float* kb = reinterpret_cast<const float*>(rslot(Sc) + w * RG::SLOTB);
     const float* vb = kb + RG::CHB / 4;
     const int j0 = k_lo + ch * RG::CH;
-    float kv[kGroup][kCols], vv[kGroup][kCols];
+    float kv[kGroup][COLS], vv[kGroup][COLS];
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
-      load_cols(kb + g * D + cc * kCols, kv[g]);
-      load_cols(vb + g * D + cc * kCols, vv[g]);
+      load_cols(kb + g * D + cc * COLS, kv[g]);
+      load_cols(vb + g * D + cc * COLS, vv[g]);
     }
 #pragma unroll
     for (int g = 0; g < kGroup; ++g) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) {
+      for (int x = 0; x < COLS; ++x) {
         s = fmaf(qr[x], kv[g][x], s);
         dp = fmaf(gr[x], vv[g][x], dp);
       }
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
       const bool vis = j < k_hi && !(CAUSAL && j > qi);
       const float ds = vis ? exp2f(s * c - lse2) * (dp - Di) : 0.f;
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) aq[x] = fmaf(ds, kv[g][x], aq[x]);
+      for (int x = 0; x < COLS; ++x) aq[x] = fmaf(ds, kv[g][x], aq[x]);
     }
   };
   if (nch > 0) {
@@ -545,17 +545,17 @@ __global__ __launch_bounds__(64 * kWaves) void bwd_dq_f32_kernel(
     wait_vm<0>();
   }
 #pragma unroll
-  for (int x = 0; x < kCols; ++x) sq[w][lane][x] = aq[x];
+  for (int x = 0; x < COLS; ++x) sq[w][lane][x] = aq[x];
   __syncthreads();
   if (w == 0 && valid) {
-    float t[kCols];
+    float t[COLS];
 #pragma unroll
-    for (int x = 0; x < kCols; ++x) t[x] = sq[0][lane][x];
+    for (int x = 0; x < COLS; ++x) t[x] = sq[0][lane][x];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww)
 #pragma unroll
-      for (int x = 0; x < kCols; ++x) t[x] += sq[ww][lane][x];
-    store_cols(dQ + qrow * D + cc * kCols, t, scale);
+      for (int x = 0; x < COLS; ++x) t[x] += sq[ww][lane][x];
+    store_cols(dQ + qrow * D + cc * COLS, t, scale);
   }
 }
 
@@ -606,28 +606,47 @@ hipError_t fwd_launch(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t bwd_launch(const BwdArgs& a, unsigned stages, hipStream_t stream) {
-  using T = F32Tile<D>;
-  const int64_t rows = (int64_t)a.BH * a.Lq;
+template <int D, bool CAUSAL, int COLS>
+void bwd_launch_cols(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+  using T = F32Tile<D, COLS>;
   const auto* Q = static_cast<const float*>(a.Q);
   const auto* K = static_cast<const float*>(a.K);
   const auto* V = static_cast<const float*>(a.V);
   const auto* G = static_cast<const float*>(a.dO);
-  if ((stages & kBwdPrepare) && rows > 0)
-    hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const float*>(a.O), G, a.lse, a.Dvec, a.lse2, rows);
   const int n_kt = (a.Lk + T::RPW - 1) / T::RPW;
   if ((stages & kBwdDkDv) && n_kt > 0)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.BH)),
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, COLS>), dim3((unsigned)(n_kt * a.BH)),
                        dim3(64 * kWaves), 0, stream, Q, K, V, G, a.lse2, a.Dvec,
                        static_cast<float*>(a.dK), static_cast<float*>(a.dV), a.BH, a.Lq, a.Lk,
                        a.scale * kLog2e, a.scale);
   const int n_qt = (a.Lq + T::RPW - 1) / T::RPW;
   if ((stages & kBwdDq) && n_qt > 0)
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.BH)),
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, COLS>), dim3((unsigned)(n_qt * a.BH)),
                        dim3(64 * kWaves), 0, stream, Q, K, V, G, a.lse2, a.Dvec,
                        static_cast<float*>(a.dQ), a.BH, a.Lq, a.Lk, a.scale * kLog2e, a.scale);
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_launch(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.BH * a.Lq;
+  const auto* G = static_cast<const float*>(a.dO);
+  if ((stages & kBwdPrepare) && rows > 0)
+    hipLaunchKernelGGL((bwd_pre_f32_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const float*>(a.O), G, a.lse, a.Dvec, a.lse2, rows);
+  // Grids smaller than the chip spread each row over more lanes, as the
+  // forward does: the fewest columns per lane (4 or 8) whose larger grid of
+  // the two kernels still fits the chip in one round.
+  const int64_t lmax = a.Lq > a.Lk ? a.Lq : a.Lk;
+  auto wgs = [&](auto COLSc) {
+    using T = F32Tile<D, decltype(COLSc)::value>;
+    return (lmax + T::RPW - 1) / T::RPW * a.BH;
+  };
+  if (wgs(IC<kCols>{}) < kComputeUnits && wgs(IC<4>{}) <= kComputeUnits)
+    bwd_launch_cols<D, CAUSAL, 4>(a, stages, stream);
+  else if (wgs(IC<kCols>{}) < kComputeUnits && wgs(IC<8>{}) <= kComputeUnits)
+    bwd_launch_cols<D, CAUSAL, 8>(a, stages, stream);
+  else
+    bwd_launch_cols<D, CAUSAL, kCols>(a, stages, stream);
   return hipGetLastError();
 }
 

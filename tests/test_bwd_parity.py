@@ -49,8 +49,14 @@ def test_bf16_small_shapes(shape, causal):
     _assert_grads(got, ref, BF16_GRAD_REL, f"{shape} causal={causal}")
 
 
+# The launcher picks 4, 8 or 16 columns per lane by grid size: 4 for
+# (1, 2, 1, 1, 64), (1, 2, 200, 130, 64) and (1, 1, 128, 100, 128); 8 for
+# (2, 1, 65, 300, 128) and (1, 3, 601, 601, 64) (ragged); 16 for (1, 8, 512,
+# 512, 64).
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(1, 2, 1, 1, 64), (2, 1, 65, 300, 128), (1, 2, 200, 130, 64)],
+@pytest.mark.parametrize("shape", [(1, 2, 1, 1, 64), (2, 1, 65, 300, 128), (1, 2, 200, 130, 64),
+                                   (1, 1, 128, 100, 128), (1, 3, 601, 601, 64),
+                                   (1, 8, 512, 512, 64)],
                          ids=lambda s: "B{}H{}Lq{}Lk{}d{}".format(*s))
 def test_f32_small_shapes(shape, causal):
     B, H, Lq, Lk, d = shape
